@@ -1,0 +1,220 @@
+/*
+ * wa.h -- C ABI of the paged-KV retrieval attention library (libwa.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library runs the attention step of block-diffusion video generation
+ * over a paged KV cache, in four calls:
+ *
+ *   wa_append_page     copy one page of K/V into the pool and record its
+ *                      mean key;
+ *   wa_select_pages    score the chunk's mean query against the page mean
+ *                      keys and keep the top-K_p pages (optionally after a
+ *                      prompt stage that picks the candidate chunks);
+ *   wa_gather          copy the kept pages into one contiguous K/V buffer;
+ *   wa_block_attention unmasked softmax attention of the chunk's queries over
+ *                      the gathered pages followed by the chunk's own K/V.
+ *
+ * Sources (page title, section):
+ *   WorldAttention review, "WorldAttention: An Efficient Attention
+ *   Architecture for Interactive Video World Models" (jaehun.me):
+ *     - "HKV: Page-Level Multi-Tier Memory": a page is 8 latent frames of
+ *       1,560 tokens; the prompt stage ranks past chunks by cosine
+ *       similarity of prompt embeddings; the page stage ranks pages by
+ *       alpha = mean(Q)^T mean(K_page) / sqrt(d_k) and keeps K_p = 4;
+ *     - "Core Idea", item 3: retrieved pages are reorganised into one
+ *       contiguous buffer.
+ *   Inferix summary, "Inferix: A Block-Diffusion based Next-Generation
+ *   Inference Engine for World Simulation", section 3.4, "The
+ *   Block-Diffusion Generation Pipeline", Step 3: a block's queries attend
+ *   over [cached K ++ own K] and [cached V ++ own V] with one softmax and no
+ *   mask inside the block; Step 4: the cache grows only after the block's
+ *   last denoising step.
+ *
+ * Conventions shared by every call
+ *   - Memory: every array argument is DEVICE memory owned by the caller,
+ *     except the wa_layout / wa_prompt_stage structs themselves, which are
+ *     host memory read during the call only.  The library allocates and frees
+ *     nothing and keeps no global state; calls are reentrant.
+ *   - Layout: token-major and dense.  A K, V, Q or output array of T tokens
+ *     is [T][n_heads][head_dim]; the pool is [max_pages][page_tokens][n_heads]
+ *     [head_dim]; page_means is [max_pages][n_heads][head_dim] double.
+ *   - Element type: layout.dtype (WA_F32 = float, WA_BF16 = bfloat16) for
+ *     pages, queries and own K/V.  Means, scores and the selection are fp64.
+ *   - Alignment: every device pointer is 16-byte aligned, and one token row
+ *     (n_heads * head_dim elements) is a multiple of 16 bytes.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Every
+ *     call only enqueues work on it and returns; no call synchronises the
+ *     host, and page indices never travel to the host.  Buffers must stay
+ *     valid until the stream has finished the work.
+ *   - Errors: argument errors are found on the host before anything is
+ *     enqueued and return WA_ERR_INVALID_ARG or WA_ERR_UNSUPPORTED; a failed
+ *     launch returns WA_ERR_HIP.  Nothing aborts or throws.  Device data
+ *     (candidate ids, page indices) are checked on the device: an id outside
+ *     [0, max_pages) is never dereferenced (see each call).
+ */
+#ifndef WA_H
+#define WA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t wa_status;
+#define WA_OK 0
+#define WA_ERR_INVALID_ARG (-1)
+#define WA_ERR_UNSUPPORTED (-2)
+#define WA_ERR_HIP (-3)
+
+/* element types */
+#define WA_F32 0
+#define WA_BF16 1
+
+/* Largest n_heads * head_dim the kernels accept (WA_ERR_UNSUPPORTED above). */
+#define WA_MAX_ROW_ELEMS 4096
+/* Largest candidate count of one selection (WA_ERR_UNSUPPORTED above). */
+#define WA_MAX_CANDIDATES 4096
+
+typedef struct wa_layout {
+    int32_t n_heads;     /* H >= 1 */
+    int32_t head_dim;    /* d >= 1 (attention: 64 or 128 for WA_F32, 128 for WA_BF16) */
+    int32_t page_tokens; /* P_t >= 1 tokens per page (8 frames x 1,560 = 12,480 in the pages) */
+    int32_t max_pages;   /* pool slots >= 1 */
+    int32_t dtype;       /* WA_F32 or WA_BF16 */
+} wa_layout;
+
+/*
+ * Prompt stage (WorldAttention review, "HKV: Page-Level Multi-Tier Memory",
+ * stage 1, with several kept chunks as in the Tab. 8 ablation): rank the
+ * past chunks by cos(cur_prompt, chunk_prompts[m]) descending, ties to the
+ * lower chunk id; keep the first n_keep; the candidate pages are their pages,
+ * chunk by chunk in rank order, page by page in chunk_pages order.
+ */
+typedef struct wa_prompt_stage {
+    const float *chunk_prompts;  /* device [n_chunks][emb_dim] */
+    const float *cur_prompt;     /* device [emb_dim] */
+    const int32_t *chunk_pages;  /* device [n_chunks][pages_per_chunk] pool slots */
+    int32_t n_chunks;            /* 1 ... WA_MAX_CANDIDATES */
+    int32_t emb_dim;             /* >= 1 */
+    int32_t pages_per_chunk;     /* >= 1 */
+    int32_t n_keep;              /* 1 ... n_chunks */
+    int32_t *out_chunks;         /* device [n_keep] kept chunk ids in rank order, or NULL */
+    int32_t *out_cand;           /* device [n_keep * pages_per_chunk] candidate pages, or NULL */
+} wa_prompt_stage;
+
+/*
+ * Bytes of device workspace wa_append_page needs for this layout (0 if the
+ * layout is invalid).  Contents need no initialisation.
+ */
+size_t wa_append_workspace_bytes(const wa_layout *layout);
+
+/*
+ * Append one page (WorldAttention review, "HKV: Page-Level Multi-Tier
+ * Memory": a page's keys are summarised by their mean; Inferix summary,
+ * section 3.4, Step 4: pages enter the cache after the block is final).
+ *
+ *   k_pool[slot] = k_src, v_pool[slot] = v_src               (byte copies)
+ *   page_means[slot][h][c] = (sum_t k_src[t][h][c]) / page_tokens   (fp64)
+ *
+ * k_src, v_src: [page_tokens][H][d].  If k_src (v_src) is the address of
+ * pool slot `slot` itself, that copy is skipped ("mean-only": the producer
+ * wrote the page in place).  v_src may be NULL: V is then left untouched.
+ * Any other overlap of source and pool is undefined.  The sum is
+ * accumulated in fp64 in a fixed order, so repeated calls are bitwise equal.
+ * workspace: device, >= wa_append_workspace_bytes(layout) bytes.
+ * Errors: NULL layout / k_src / k_pool / page_means / workspace, slot outside
+ * [0, max_pages), workspace too small -> WA_ERR_INVALID_ARG; unsupported
+ * layout -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_append_page(const wa_layout *layout, const void *k_src, const void *v_src,
+                         void *k_pool, void *v_pool, int32_t slot, double *page_means,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace wa_select_pages needs (0 if the arguments are
+ * invalid).  prompt may be NULL.  Contents need no initialisation.
+ */
+size_t wa_select_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_cand,
+                                 const wa_prompt_stage *prompt);
+
+/*
+ * Page stage (WorldAttention review, "HKV: Page-Level Multi-Tier Memory",
+ * stage 2), all in fp64:
+ *   qbar[h][c]  = (sum_i q[i][h][c]) / n_q
+ *   alpha_j     = (sum_h sum_c qbar[h][c] * page_means[cand[j]][h][c]) / sqrt(d)
+ *   out_idx[r]  = the candidate ranked r-th by (alpha desc, page id asc), r < k_p.
+ * One score per page, shared by all heads.
+ *
+ * q: [n_q][H][d].  cand: device [n_cand] pool slots; NULL means slots
+ * 0 ... n_cand-1.  prompt: NULL, or a prompt stage that produces the
+ * candidates (then cand must be NULL and n_cand = n_keep * pages_per_chunk).
+ * out_idx: device [k_p] int32.  out_scores: device [n_cand] double (alpha in
+ * candidate order), or NULL.  A candidate id outside [0, max_pages) is never
+ * read: it scores -inf and ranks last; ranks that only such ids could fill
+ * get -1.  Duplicate ids are distinct candidates.
+ * Errors: NULL layout / q / page_means / out_idx / workspace, n_q < 1,
+ * n_cand < 1, k_p < 1 or k_p > n_cand, inconsistent prompt stage, workspace
+ * too small -> WA_ERR_INVALID_ARG; n_cand or n_chunks > WA_MAX_CANDIDATES,
+ * unsupported layout -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_select_pages(const wa_layout *layout, const void *q, int32_t n_q,
+                          const double *page_means, const int32_t *cand, int32_t n_cand,
+                          const wa_prompt_stage *prompt, int32_t k_p, int32_t *out_idx,
+                          double *out_scores, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * Gather (WorldAttention review, "Core Idea", item 3: the retrieved pages are
+ * reorganised into one contiguous buffer):
+ *   k_ctx[r * page_tokens + t] = k_pool[idx[r]][t]    for r < k_p, t < page_tokens
+ * and the same for V; byte copies, pages in the order of idx.
+ *
+ * idx: device [k_p] int32, read on the device (no host synchronisation).
+ * k_ctx, v_ctx: [k_p * page_tokens][H][d].  v_pool and v_ctx may both be
+ * NULL (K only).  A rank whose idx is outside [0, max_pages) is left
+ * unwritten.  The pool and the destination must not overlap.
+ * Errors: NULL layout / k_pool / idx / k_ctx, only one of v_pool / v_ctx NULL,
+ * k_p < 1 -> WA_ERR_INVALID_ARG; unsupported layout -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_gather(const wa_layout *layout, const void *k_pool, const void *v_pool,
+                    const int32_t *idx, int32_t k_p, void *k_ctx, void *v_ctx, void *stream);
+
+/*
+ * Block attention (Inferix summary, section 3.4, Step 3; the einsum post on
+ * nakranivaibhav.github.io, "Where the mental model stops": scores are the
+ * contraction over d, softmax and the value weighting follow it).  For head
+ * h and query row i, with keys n running over the n_ctx rows of k_ctx and
+ * then the n_own rows of k_own (values likewise):
+ *   s_n   = (q[i][h] . k_n[h]) * softmax_scale
+ *   out[i][h] = sum_n exp(s_n) v_n[h] / sum_n exp(s_n)
+ *   lse[h][i] = log(sum_n exp(s_n))                 (natural log)
+ * One softmax over both segments, no mask of any kind.
+ *
+ * q, out: [n_q][H][d]; k_ctx, v_ctx: [n_ctx][H][d]; k_own, v_own: [n_own][H][d].
+ * WA_BF16 inputs are multiplied on the matrix cores with fp32 accumulation;
+ * the probabilities are rounded to bf16 before the value product.
+ * out_dtype: WA_F32, or WA_BF16 when layout.dtype is WA_BF16.
+ * lse: device [H][n_q] float, or NULL.  n_ctx or n_own may be 0 (the
+ * matching pointers may then be NULL).  out must not overlap any input.
+ * page_tokens and max_pages of the layout are not used.
+ * Errors: NULL layout / q / out, NULL pointers of a non-empty segment,
+ * n_q < 1, n_ctx < 0, n_own < 0, n_ctx + n_own < 1, non-finite
+ * softmax_scale -> WA_ERR_INVALID_ARG; head_dim or out_dtype not supported
+ * for the dtype -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_block_attention(const wa_layout *layout, const void *q, int32_t n_q,
+                             const void *k_ctx, const void *v_ctx, int32_t n_ctx,
+                             const void *k_own, const void *v_own, int32_t n_own,
+                             float softmax_scale, int32_t out_dtype, void *out, float *lse,
+                             void *stream);
+
+/* Static text describing a status code. */
+const char *wa_status_string(wa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WA_H */

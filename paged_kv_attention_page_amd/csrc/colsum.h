@@ -1,0 +1,98 @@
+// Column sums of a token-major [rows][hd] array, in fp64, with a fixed
+// summation order.  Used for the page mean key (append) and the chunk mean
+// query (select): WorldAttention review, "HKV: Page-Level Multi-Tier Memory",
+// page stage.
+//
+// Work split: block b owns rows [b*rows_per_block, ...).  Thread t owns the
+// 16-byte column vector c = t % chunks and the rows r == t / chunks (mod
+// row_lanes) of the block's range, accumulating in registers (row order).
+// The row_lanes partials of a column are then added in lane order through
+// LDS, and one fp64 partial per (block, column) goes to the workspace.  A
+// second kernel adds the block partials in block order.  The inputs are bf16
+// or fp32 values, so in practice every fp64 sum here is exact; the fixed
+// order makes repeated calls bitwise equal regardless.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wa {
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Add the elements of one 16-byte vector to acc[] (8 bf16 or 4 fp32 values).
+template <bool BF16>
+__device__ __forceinline__ void accumulate_vec(double *acc, uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (BF16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[2 * j] += (double)bf16lo(w[j]);
+            acc[2 * j + 1] += (double)bf16hi(w[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += (double)__uint_as_float(w[j]);
+    }
+}
+
+// One block's share of the column sums, optionally copying the rows of up to
+// two arrays (K and V of a page) to their destinations on the way.
+//   x      [rows][chunks] 16-byte vectors, summed (and copied to x_dst if set)
+//   y      [rows][chunks] vectors copied to y_dst (not summed), or null
+//   lds    row_lanes * chunks * VEC doubles of shared memory
+//   part   [chunks * VEC] doubles: this block's partial sums
+template <bool BF16>
+__device__ __forceinline__ void colsum_block(const uint4 *__restrict__ x, uint4 *__restrict__ x_dst,
+                                             const uint4 *__restrict__ y, uint4 *__restrict__ y_dst,
+                                             int64_t rows, int chunks, int row_lanes,
+                                             int rows_per_block, int block, double *lds,
+                                             double *__restrict__ part) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    const int t = threadIdx.x;
+    const int hd = chunks * VEC;
+    const int64_t r0 = (int64_t)block * rows_per_block;
+    const int64_t r1 = min(rows, r0 + rows_per_block);
+    double acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+
+    if (t < chunks * row_lanes) {
+        const int c = t % chunks;
+        const int lane = t / chunks;
+        int64_t r = r0 + lane;
+        // four rows in flight per thread
+        for (; r + 3 * row_lanes < r1; r += 4 * row_lanes) {
+            uint4 xv[4], yv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xv[u] = x[(r + u * row_lanes) * chunks + c];
+            if (y) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) yv[u] = y[(r + u * row_lanes) * chunks + c];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (x_dst) x_dst[(r + u * row_lanes) * chunks + c] = xv[u];
+                if (y) y_dst[(r + u * row_lanes) * chunks + c] = yv[u];
+                accumulate_vec<BF16>(acc, xv[u]);
+            }
+        }
+        for (; r < r1; r += row_lanes) {
+            const uint4 xv = x[r * chunks + c];
+            if (x_dst) x_dst[r * chunks + c] = xv;
+            if (y) y_dst[r * chunks + c] = y[r * chunks + c];
+            accumulate_vec<BF16>(acc, xv);
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lds[lane * hd + c * VEC + e] = acc[e];
+    }
+    __syncthreads();
+    for (int col = t; col < hd; col += blockDim.x) {
+        double s = 0.0;
+        for (int lane = 0; lane < row_lanes; ++lane) s += lds[lane * hd + col];
+        part[col] = s;
+    }
+}
+
+}  // namespace wa

@@ -1,0 +1,98 @@
+// Append one page to the pool and record its mean key (WorldAttention
+// review, "HKV: Page-Level Multi-Tier Memory": each page is summarised by the
+// mean of its keys; Inferix summary, section 3.4, Step 4: the cache grows
+// after a block's last denoising step).
+//
+// Pass 1 (k_append_sum): one HBM pass over the page.  Every block copies its
+// row range of K (and V) into the pool slot and forms fp64 partial column
+// sums of K.  Pass 2 (k_colsum_finish): adds the block partials in block
+// order and divides by the row count.  Bound: HBM bandwidth; the algorithmic
+// traffic is 2 x (K + V page bytes) plus 8 bytes per mean element written.
+#include "colsum.h"
+#include "wa_internal.h"
+
+namespace wa {
+
+ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int max_blocks, int min_rows) {
+    ColSumPlan p;
+    p.vec = 16 / elem_bytes(dtype);
+    p.chunks = (int)(hd / p.vec);
+    int lanes = 512 / p.chunks;
+    const int lds_cap = (int)(49152 / (hd * 8));
+    if (lanes > lds_cap) lanes = lds_cap;
+    if (lanes < 1) lanes = 1;
+    p.row_lanes = lanes;
+    p.threads = p.chunks * lanes;
+    if (p.threads < 64) p.threads = 64;
+    p.threads = (p.threads + 63) / 64 * 64;
+    int64_t blocks = (rows + min_rows - 1) / min_rows;
+    if (blocks > max_blocks) blocks = max_blocks;
+    if (blocks < 1) blocks = 1;
+    p.rows_per_block = (int)((rows + blocks - 1) / blocks);
+    p.blocks = (int)((rows + p.rows_per_block - 1) / p.rows_per_block);
+    return p;
+}
+
+static ColSumPlan append_plan(int32_t dtype, int64_t hd, int64_t page_tokens) {
+    return colsum_plan(dtype, hd, page_tokens, 1024, 32);
+}
+
+size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens) {
+    const ColSumPlan p = append_plan(dtype, hd, page_tokens);
+    return (size_t)p.blocks * (size_t)hd * sizeof(double);
+}
+
+template <bool BF16>
+__global__ void k_append_sum(const uint4 *__restrict__ k_src, uint4 *__restrict__ k_dst,
+                             const uint4 *__restrict__ v_src, uint4 *__restrict__ v_dst,
+                             int64_t rows, int chunks, int row_lanes, int rows_per_block,
+                             double *__restrict__ partial) {
+    extern __shared__ double lds[];
+    constexpr int VEC = BF16 ? 8 : 4;
+    colsum_block<BF16>(k_src, k_dst, v_src, v_dst, rows, chunks, row_lanes, rows_per_block,
+                       blockIdx.x, lds, partial + (int64_t)blockIdx.x * chunks * VEC);
+}
+
+// out[col] = (sum over blocks b in order of partial[b][col]) / rows
+__global__ void k_colsum_finish(const double *__restrict__ partial, int blocks, int hd,
+                                int64_t rows, double *__restrict__ out) {
+    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= hd) return;
+    double s = 0.0;
+    for (int b = 0; b < blocks; ++b) s += partial[(int64_t)b * hd + col];
+    out[col] = s / (double)rows;
+}
+
+hipError_t launch_append(const wa_layout &L, const void *k_src, const void *v_src, void *k_pool,
+                         void *v_pool, int32_t slot, double *page_means, void *ws,
+                         hipStream_t s) {
+    const int64_t hd = (int64_t)L.n_heads * L.head_dim;
+    const int64_t page_elems = (int64_t)L.page_tokens * hd;
+    const int eb = elem_bytes(L.dtype);
+    char *k_slot = (char *)k_pool + (int64_t)slot * page_elems * eb;
+    char *v_slot = v_pool ? (char *)v_pool + (int64_t)slot * page_elems * eb : nullptr;
+    // a source that already is the slot needs no copy (the mean-only mode)
+    uint4 *k_dst = (k_src == k_slot) ? nullptr : (uint4 *)k_slot;
+    const uint4 *v_read = (v_src && v_src != v_slot && v_slot) ? (const uint4 *)v_src : nullptr;
+    uint4 *v_dst = v_read ? (uint4 *)v_slot : nullptr;
+
+    const ColSumPlan p = append_plan(L.dtype, hd, L.page_tokens);
+    const size_t lds = (size_t)p.row_lanes * hd * sizeof(double);
+    double *partial = (double *)ws;
+    if (L.dtype == WA_BF16)
+        hipLaunchKernelGGL(k_append_sum<true>, dim3(p.blocks), dim3(p.threads), lds, s,
+                           (const uint4 *)k_src, k_dst, v_read, v_dst, (int64_t)L.page_tokens,
+                           p.chunks, p.row_lanes, p.rows_per_block, partial);
+    else
+        hipLaunchKernelGGL(k_append_sum<false>, dim3(p.blocks), dim3(p.threads), lds, s,
+                           (const uint4 *)k_src, k_dst, v_read, v_dst, (int64_t)L.page_tokens,
+                           p.chunks, p.row_lanes, p.rows_per_block, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_colsum_finish, dim3((unsigned)((hd + 255) / 256)), dim3(256), 0, s,
+                       (const double *)partial, p.blocks, (int)hd, (int64_t)L.page_tokens,
+                       page_means + (int64_t)slot * hd);
+    return hipGetLastError();
+}
+
+}  // namespace wa

@@ -1,0 +1,155 @@
+// Host entry points of libwa.so: argument validation, then kernel launches
+// on the caller's stream.  Validation runs before any HIP call, so every
+// error path can be exercised without a GPU.  Semantics and error rules of
+// each entry point are stated in include/wa.h.
+#include <math.h>
+
+#include "wa_internal.h"
+
+using namespace wa;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by all calls.  need_pool: page_tokens and max_pages matter.
+wa_status check_layout(const wa_layout *L, bool need_pool) {
+    if (!L) return WA_ERR_INVALID_ARG;
+    if (L->n_heads < 1 || L->head_dim < 1) return WA_ERR_INVALID_ARG;
+    if (L->dtype != WA_F32 && L->dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
+    if (need_pool && (L->page_tokens < 1 || L->max_pages < 1)) return WA_ERR_INVALID_ARG;
+    const int64_t hd = (int64_t)L->n_heads * L->head_dim;
+    if (hd > WA_MAX_ROW_ELEMS) return WA_ERR_UNSUPPORTED;
+    if ((hd * elem_bytes(L->dtype)) % 16 != 0) return WA_ERR_UNSUPPORTED;
+    return WA_OK;
+}
+
+wa_status from_hip(hipError_t e) { return e == hipSuccess ? WA_OK : WA_ERR_HIP; }
+
+wa_status check_prompt(const wa_layout *L, const wa_prompt_stage *P, const int32_t *cand,
+                       int32_t n_cand) {
+    if (!P) return WA_OK;
+    if (cand) return WA_ERR_INVALID_ARG;
+    if (!P->chunk_prompts || !P->cur_prompt || !P->chunk_pages) return WA_ERR_INVALID_ARG;
+    if (!aligned16(P->chunk_prompts) || !aligned16(P->cur_prompt) || !aligned16(P->chunk_pages))
+        return WA_ERR_INVALID_ARG;
+    if (P->n_chunks < 1 || P->emb_dim < 1 || P->pages_per_chunk < 1 || P->n_keep < 1 ||
+        P->n_keep > P->n_chunks)
+        return WA_ERR_INVALID_ARG;
+    if (P->n_chunks > WA_MAX_CANDIDATES) return WA_ERR_UNSUPPORTED;
+    if ((int64_t)P->n_keep * P->pages_per_chunk != n_cand) return WA_ERR_INVALID_ARG;
+    (void)L;
+    return WA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wa_append_workspace_bytes(const wa_layout *L) {
+    if (check_layout(L, true) != WA_OK) return 0;
+    return append_workspace_bytes(L->dtype, (int64_t)L->n_heads * L->head_dim, L->page_tokens);
+}
+
+wa_status wa_append_page(const wa_layout *L, const void *k_src, const void *v_src, void *k_pool,
+                         void *v_pool, int32_t slot, double *page_means, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    wa_status st = check_layout(L, true);
+    if (st != WA_OK) return st;
+    if (!k_src || !k_pool || !page_means || !workspace) return WA_ERR_INVALID_ARG;
+    if (v_src && !v_pool) return WA_ERR_INVALID_ARG;
+    if (slot < 0 || slot >= L->max_pages) return WA_ERR_INVALID_ARG;
+    if (!aligned16(k_src) || !aligned16(k_pool) || !aligned16(page_means) || !aligned16(workspace) ||
+        (v_src && !aligned16(v_src)) || (v_pool && !aligned16(v_pool)))
+        return WA_ERR_INVALID_ARG;
+    if (workspace_bytes < wa_append_workspace_bytes(L)) return WA_ERR_INVALID_ARG;
+    return from_hip(launch_append(*L, k_src, v_src, k_pool, v_pool, slot, page_means, workspace,
+                                  (hipStream_t)stream));
+}
+
+size_t wa_select_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_cand,
+                                 const wa_prompt_stage *prompt) {
+    if (check_layout(L, true) != WA_OK || n_q < 1 || n_cand < 1) return 0;
+    if (n_cand > WA_MAX_CANDIDATES) return 0;
+    const int32_t n_chunks = prompt ? prompt->n_chunks : 0;
+    if (n_chunks < 0 || n_chunks > WA_MAX_CANDIDATES) return 0;
+    return select_workspace(L->dtype, (int64_t)L->n_heads * L->head_dim, n_q, n_cand, n_chunks)
+        .total;
+}
+
+wa_status wa_select_pages(const wa_layout *L, const void *q, int32_t n_q, const double *page_means,
+                          const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
+                          int32_t k_p, int32_t *out_idx, double *out_scores, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    wa_status st = check_layout(L, true);
+    if (st != WA_OK) return st;
+    if (!q || !page_means || !out_idx || !workspace) return WA_ERR_INVALID_ARG;
+    if (n_q < 1 || n_cand < 1 || k_p < 1 || k_p > n_cand) return WA_ERR_INVALID_ARG;
+    if (n_cand > WA_MAX_CANDIDATES) return WA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(page_means) || !aligned16(out_idx) || !aligned16(workspace) ||
+        (cand && !aligned16(cand)) || (out_scores && !aligned16(out_scores)))
+        return WA_ERR_INVALID_ARG;
+    st = check_prompt(L, prompt, cand, n_cand);
+    if (st != WA_OK) return st;
+    if (workspace_bytes < wa_select_workspace_bytes(L, n_q, n_cand, prompt))
+        return WA_ERR_INVALID_ARG;
+    return from_hip(launch_select(*L, q, n_q, page_means, cand, n_cand, prompt, k_p, out_idx,
+                                  out_scores, workspace, (hipStream_t)stream));
+}
+
+wa_status wa_gather(const wa_layout *L, const void *k_pool, const void *v_pool, const int32_t *idx,
+                    int32_t k_p, void *k_ctx, void *v_ctx, void *stream) {
+    wa_status st = check_layout(L, true);
+    if (st != WA_OK) return st;
+    if (!k_pool || !idx || !k_ctx) return WA_ERR_INVALID_ARG;
+    if ((v_pool == nullptr) != (v_ctx == nullptr)) return WA_ERR_INVALID_ARG;
+    if (k_p < 1) return WA_ERR_INVALID_ARG;
+    if (k_p > 65535) return WA_ERR_UNSUPPORTED;
+    if (!aligned16(k_pool) || !aligned16(k_ctx) || (v_pool && !aligned16(v_pool)) ||
+        (v_ctx && !aligned16(v_ctx)) || ((uintptr_t)idx & 3u))
+        return WA_ERR_INVALID_ARG;
+    return from_hip(launch_gather(*L, k_pool, v_pool, idx, k_p, k_ctx, v_ctx, (hipStream_t)stream));
+}
+
+wa_status wa_block_attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
+                             const void *v_ctx, int32_t n_ctx, const void *k_own,
+                             const void *v_own, int32_t n_own, float softmax_scale,
+                             int32_t out_dtype, void *out, float *lse, void *stream) {
+    wa_status st = check_layout(L, false);
+    if (st != WA_OK) return st;
+    if (!q || !out) return WA_ERR_INVALID_ARG;
+    if (n_q < 1 || n_ctx < 0 || n_own < 0 || (int64_t)n_ctx + n_own < 1) return WA_ERR_INVALID_ARG;
+    if ((int64_t)n_ctx + n_own > 0x7fffffff - 256) return WA_ERR_UNSUPPORTED;
+    if (n_ctx > 0 && (!k_ctx || !v_ctx)) return WA_ERR_INVALID_ARG;
+    if (n_own > 0 && (!k_own || !v_own)) return WA_ERR_INVALID_ARG;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || (n_ctx > 0 && (!aligned16(k_ctx) || !aligned16(v_ctx))) ||
+        (n_own > 0 && (!aligned16(k_own) || !aligned16(v_own))) || ((uintptr_t)lse & 3u))
+        return WA_ERR_INVALID_ARG;
+    if (L->dtype == WA_F32) {
+        if (L->head_dim != 64 && L->head_dim != 128) return WA_ERR_UNSUPPORTED;
+        if (out_dtype != WA_F32) return WA_ERR_UNSUPPORTED;
+        return from_hip(launch_attention_f32(L->n_heads, L->head_dim, (const float *)q, n_q,
+                                             (const float *)k_ctx, (const float *)v_ctx, n_ctx,
+                                             (const float *)k_own, (const float *)v_own, n_own,
+                                             softmax_scale, (float *)out, lse, (hipStream_t)stream));
+    }
+    if (L->head_dim != 128) return WA_ERR_UNSUPPORTED;
+    if (out_dtype != WA_F32 && out_dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
+    return from_hip(launch_attention_bf16(L->n_heads, (const uint16_t *)q, n_q,
+                                          (const uint16_t *)k_ctx, (const uint16_t *)v_ctx, n_ctx,
+                                          (const uint16_t *)k_own, (const uint16_t *)v_own, n_own,
+                                          softmax_scale, out_dtype, out, lse, (hipStream_t)stream));
+}
+
+const char *wa_status_string(wa_status s) {
+    switch (s) {
+        case WA_OK: return "ok";
+        case WA_ERR_INVALID_ARG: return "invalid argument";
+        case WA_ERR_UNSUPPORTED: return "unsupported layout or argument";
+        case WA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

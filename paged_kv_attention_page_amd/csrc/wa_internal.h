@@ -1,0 +1,79 @@
+// Internal declarations shared by the host entry points (wa_api.cpp) and the
+// kernel sources.  Not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/wa.h"
+
+namespace wa {
+
+inline int elem_bytes(int32_t dtype) { return dtype == WA_F32 ? 4 : 2; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// column sums (page mean key, chunk mean query)
+//
+// A column-sum launch splits the rows of a [rows][hd] array into `blocks`
+// row ranges; each block writes one fp64 partial sum per column, and a second
+// kernel adds the partials in block order.  `vec` = elements per 16-byte
+// vector, `chunks` = hd / vec vectors per row, `row_lanes` = rows read at once.
+struct ColSumPlan {
+    int vec;
+    int chunks;
+    int row_lanes;
+    int threads;
+    int rows_per_block;
+    int blocks;
+};
+ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int max_blocks, int min_rows);
+
+// ---------------------------------------------------------------------------
+// workspace layouts
+
+size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens);
+
+struct SelectWs {
+    size_t partial_q;   // [q_blocks][hd] double
+    size_t cosine;      // [n_chunks] double
+    size_t alpha_part;  // [groups][n_cand] double
+    size_t cand;        // [n_cand] int32
+    size_t total;
+    ColSumPlan q_plan;
+    int groups;
+};
+SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
+                          int32_t n_chunks);
+
+// ---------------------------------------------------------------------------
+// launchers (return hipSuccess or the launch error)
+
+hipError_t launch_append(const wa_layout &L, const void *k_src, const void *v_src, void *k_pool,
+                         void *v_pool, int32_t slot, double *page_means, void *ws,
+                         hipStream_t s);
+
+hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const double *page_means,
+                         const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
+                         int32_t k_p, int32_t *out_idx, double *out_scores, void *ws,
+                         hipStream_t s);
+
+hipError_t launch_gather(const wa_layout &L, const void *k_pool, const void *v_pool,
+                         const int32_t *idx, int32_t k_p, void *k_ctx, void *v_ctx,
+                         hipStream_t s);
+
+hipError_t launch_attention_f32(int32_t n_heads, int32_t head_dim, const float *q, int32_t n_q,
+                                const float *k_ctx, const float *v_ctx, int32_t n_ctx,
+                                const float *k_own, const float *v_own, int32_t n_own,
+                                float scale, float *out, float *lse, hipStream_t s);
+
+hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q,
+                                 const uint16_t *k_ctx, const uint16_t *v_ctx, int32_t n_ctx,
+                                 const uint16_t *k_own, const uint16_t *v_own, int32_t n_own,
+                                 float scale, int32_t out_dtype, void *out, float *lse,
+                                 hipStream_t s);
+
+}  // namespace wa

@@ -1,0 +1,220 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before anything is launched.
+
+Pointers here are fake aligned addresses: every call below fails validation,
+which runs before any HIP call, so nothing touches a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_page_amd as wa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wa.h")
+
+A = ctypes.c_void_p(0x10000)        # a 16-byte aligned stand-in pointer
+B = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)      # misaligned
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(wa.library_path()):
+        pytest.skip("libwa.so not built (run __graft_entry__.build())")
+    return wa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("wa_append_page", "wa_select_pages", "wa_gather", "wa_block_attention"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), "libwa.so does not export %s" % n
+
+
+def test_status_strings(lib):
+    assert wa.wa_status_string(wa.WA_OK) == "ok"
+    for s in (wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED, wa.WA_ERR_HIP):
+        assert wa.wa_status_string(s) not in ("ok", "unknown status")
+    assert wa.wa_status_string(-99) == "unknown status"
+
+
+def L(dtype=wa.WA_BF16, H=12, d=128, pt=12480, pages=16):
+    return ctypes.byref(wa.layout(dtype, H, d, pt, pages))
+
+
+# ---------------------------------------------------------------------------
+# append
+
+def test_append_workspace_size(lib):
+    n = lib.wa_append_workspace_bytes(L())
+    assert n > 0 and n % 8 == 0
+    assert lib.wa_append_workspace_bytes(None) == 0
+    assert lib.wa_append_workspace_bytes(L(H=0)) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_layout", wa.WA_ERR_INVALID_ARG),
+    ("null_k_src", wa.WA_ERR_INVALID_ARG),
+    ("null_pool", wa.WA_ERR_INVALID_ARG),
+    ("null_means", wa.WA_ERR_INVALID_ARG),
+    ("null_ws", wa.WA_ERR_INVALID_ARG),
+    ("slot_neg", wa.WA_ERR_INVALID_ARG),
+    ("slot_big", wa.WA_ERR_INVALID_ARG),
+    ("small_ws", wa.WA_ERR_INVALID_ARG),
+    ("misaligned", wa.WA_ERR_INVALID_ARG),
+    ("v_without_pool", wa.WA_ERR_INVALID_ARG),
+    ("bad_dtype", wa.WA_ERR_UNSUPPORTED),
+    ("row_too_wide", wa.WA_ERR_UNSUPPORTED),
+    ("row_not_16B", wa.WA_ERR_UNSUPPORTED),
+])
+def test_append_rejects(lib, case, expect):
+    lay = L()
+    big = 1 << 40
+    args = dict(layout=lay, k_src=A, v_src=B, k_pool=A, v_pool=B, slot=3, means=A, ws=A, wsb=big)
+    if case == "null_layout":
+        args["layout"] = None
+    elif case == "null_k_src":
+        args["k_src"] = NULL
+    elif case == "null_pool":
+        args["k_pool"] = NULL
+    elif case == "null_means":
+        args["means"] = NULL
+    elif case == "null_ws":
+        args["ws"] = NULL
+    elif case == "slot_neg":
+        args["slot"] = -1
+    elif case == "slot_big":
+        args["slot"] = 16
+    elif case == "small_ws":
+        args["wsb"] = 8
+    elif case == "misaligned":
+        args["k_src"] = MIS
+    elif case == "v_without_pool":
+        args["v_pool"] = NULL
+    elif case == "bad_dtype":
+        args["layout"] = L(dtype=7)
+    elif case == "row_too_wide":
+        args["layout"] = L(H=64, d=128)
+    elif case == "row_not_16B":
+        args["layout"] = L(dtype=wa.WA_BF16, H=1, d=4)
+    st = lib.wa_append_page(args["layout"], args["k_src"], args["v_src"], args["k_pool"],
+                            args["v_pool"], args["slot"], args["means"], args["ws"],
+                            args["wsb"], None)
+    assert st == expect
+
+
+# ---------------------------------------------------------------------------
+# select
+
+def test_select_workspace_size(lib):
+    assert lib.wa_select_workspace_bytes(L(), 4680, 16, None) > 0
+    assert lib.wa_select_workspace_bytes(L(), 0, 16, None) == 0
+    assert lib.wa_select_workspace_bytes(L(), 4680, 0, None) == 0
+    assert lib.wa_select_workspace_bytes(L(), 4680, 5000, None) == 0
+
+
+def _select(lib, lay=None, q=A, n_q=100, means=A, cand=NULL, n_cand=16, prompt=None, k_p=4,
+            out=A, ws=A, wsb=1 << 40):
+    return lib.wa_select_pages(lay if lay is not None else L(), q, n_q, means, cand, n_cand,
+                               prompt, k_p, out, None, ws, wsb, None)
+
+
+def test_select_rejects(lib):
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert _select(lib, q=NULL) == E
+    assert _select(lib, means=NULL) == E
+    assert _select(lib, out=NULL) == E
+    assert _select(lib, ws=NULL) == E
+    assert _select(lib, n_q=0) == E
+    assert _select(lib, n_cand=0) == E
+    assert _select(lib, k_p=0) == E
+    assert _select(lib, k_p=-2) == E
+    assert _select(lib, k_p=17) == E
+    assert _select(lib, n_cand=5000, k_p=4) == U
+    assert _select(lib, wsb=16) == E
+    assert _select(lib, q=MIS) == E
+    assert _select(lib, lay=L(pages=0)) == E
+
+
+def _prompt(n_chunks=16, emb=4096, ppc=4, keep=4):
+    return wa.PromptStage(0x30000, 0x40000, 0x50000, n_chunks, emb, ppc, keep, None, None)
+
+
+def test_select_rejects_bad_prompt_stage(lib):
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    ok = _prompt()
+    # candidates given as well as a prompt stage
+    assert _select(lib, cand=B, prompt=ctypes.byref(ok)) == E
+    # n_cand must equal n_keep * pages_per_chunk
+    assert _select(lib, n_cand=12, prompt=ctypes.byref(ok)) == E
+    assert _select(lib, prompt=ctypes.byref(_prompt(keep=17))) == E
+    assert _select(lib, prompt=ctypes.byref(_prompt(keep=0))) == E
+    assert _select(lib, prompt=ctypes.byref(_prompt(emb=0))) == E
+    assert _select(lib, n_cand=4, k_p=4, prompt=ctypes.byref(_prompt(n_chunks=5000, ppc=1, keep=4))) == U
+    bad = _prompt()
+    bad.chunk_prompts = None
+    assert _select(lib, prompt=ctypes.byref(bad)) == E
+
+
+# ---------------------------------------------------------------------------
+# gather
+
+def test_gather_rejects(lib):
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    g = lib.wa_gather
+    assert g(None, A, B, A, 4, A, B, None) == E
+    assert g(L(), NULL, B, A, 4, A, B, None) == E
+    assert g(L(), A, B, NULL, 4, A, B, None) == E
+    assert g(L(), A, B, A, 4, NULL, B, None) == E
+    assert g(L(), A, NULL, A, 4, A, B, None) == E        # only one of v_pool / v_ctx
+    assert g(L(), A, B, A, 0, A, B, None) == E
+    assert g(L(), A, B, A, 70000, A, B, None) == U
+    assert g(L(), MIS, B, A, 4, A, B, None) == E
+    assert g(L(pt=0), A, B, A, 4, A, B, None) == E
+
+
+# ---------------------------------------------------------------------------
+# attention
+
+def _attn(lib, lay=None, q=A, n_q=64, kc=A, vc=B, n_ctx=64, ko=A, vo=B, n_own=64, scale=0.1,
+          odt=wa.WA_F32, out=B, lse=NULL):
+    return lib.wa_block_attention(lay if lay is not None else L(), q, n_q, kc, vc, n_ctx, ko, vo,
+                                  n_own, scale, odt, out, lse, None)
+
+
+def test_attention_rejects(lib):
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert _attn(lib, q=NULL) == E
+    assert _attn(lib, out=NULL) == E
+    assert _attn(lib, n_q=0) == E
+    assert _attn(lib, n_ctx=-1) == E
+    assert _attn(lib, n_own=-1) == E
+    assert _attn(lib, n_ctx=0, n_own=0) == E
+    assert _attn(lib, kc=NULL) == E
+    assert _attn(lib, vo=NULL) == E
+    assert _attn(lib, scale=float("nan")) == E
+    assert _attn(lib, scale=float("inf")) == E
+    assert _attn(lib, scale=0.0) == E
+    assert _attn(lib, scale=-0.5) == E
+    assert _attn(lib, q=MIS) == E
+    assert _attn(lib, lse=ctypes.c_void_p(0x10002)) == E
+    assert _attn(lib, lay=L(d=64)) == U                       # bf16 needs head_dim 128
+    assert _attn(lib, lay=L(dtype=wa.WA_F32, d=96)) == U       # fp32: 64 or 128
+    assert _attn(lib, lay=L(dtype=wa.WA_F32, d=64), odt=wa.WA_BF16) == U
+    assert _attn(lib, odt=5) == U

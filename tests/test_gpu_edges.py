@@ -1,0 +1,189 @@
+"""Edge and degenerate cases of the HIP path, against the oracle or against
+properties that hold exactly (bitwise reruns, page-order invariance, device
+handling of out-of-range ids)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_page_amd as wa
+import wa_workloads as W
+from tests.pipeline import PoolRun, say, to_bits, to_device, to_f64, wa_layout
+
+pytestmark = pytest.mark.gpu
+
+BF = W.scaled(W.WORKLOADS["wan_kp4"], name="edge_bf16", n_heads=3, frame_tokens=16,
+              page_frames=4, n_pages=5, chunk_frames=5, k_p=2)    # P_t 64, N_q 80
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wa.load_library()
+
+
+def rand_rows(wl, n, seed):
+    rng = np.random.default_rng([wl.wid, 99, seed])
+    x = rng.standard_normal((n, wl.n_heads, wl.head_dim), dtype=np.float32)
+    return W.encode(wl, x)
+
+
+def attend(wl, q, kc, vc, ko, vo, odt=None, lse=False):
+    L = wa_layout(wl)
+    dev = [to_device(x) if x is not None and x.shape[0] > 0 else None for x in (q, kc, vc, ko, vo)]
+    lse_t = torch.empty(wl.n_heads, q.shape[0], dtype=torch.float32, device="cuda") if lse else None
+    out = wa.wa_block_attention(L, *dev, wl.softmax_scale, out_dtype=odt, lse=lse_t)
+    torch.cuda.synchronize()
+    return (out, lse_t) if lse else out
+
+
+@pytest.mark.parametrize("wl", [BF, W.WORKLOADS["tiny_f32"]], ids=["bf16", "f32"])
+@pytest.mark.parametrize("n_q,n_ctx,n_own", [
+    (1, 0, 1),        # a single key
+    (1, 64, 0),       # context only, one query
+    (80, 0, 80),      # own keys only
+    (257, 128, 65),   # one query past a 256-query block, keys ragged by one
+    (33, 1, 63),      # ctx/own boundary inside the first key tile
+    (64, 191, 2),     # boundary near a tile edge
+])
+def test_attention_shapes(wl, n_q, n_ctx, n_own):
+    q = rand_rows(wl, n_q, 1)
+    kc, vc = rand_rows(wl, n_ctx, 2), rand_rows(wl, n_ctx, 3)
+    ko, vo = rand_rows(wl, n_own, 4), rand_rows(wl, n_own, 5)
+    say("attention shape", wl.name, n_q, n_ctx, n_own)
+    out, lse = attend(wl, q, kc, vc, ko, vo, odt=wa.WA_F32, lse=True)
+    ref, ref_lse = oracle.attention(q, kc if n_ctx else None, vc if n_ctx else None,
+                                    ko if n_own else None, vo if n_own else None,
+                                    wl.softmax_scale)
+    tol = 1e-5 if wl.dtype == W.F32 else 1e-2
+    assert np.abs(to_f64(out) - ref).max() <= tol
+    assert np.abs(lse.cpu().double().numpy() - ref_lse).max() <= tol
+
+
+def test_attention_unit_values_and_reruns_are_bitwise_equal():
+    wl = BF
+    q, kc, ko = rand_rows(wl, 200, 1), rand_rows(wl, 300, 2), rand_rows(wl, 70, 4)
+    ones_c = W.encode(wl, np.ones((300, wl.n_heads, wl.head_dim), np.float32))
+    ones_o = W.encode(wl, np.ones((70, wl.n_heads, wl.head_dim), np.float32))
+    say("attention unit values")
+    out = attend(wl, q, kc, ones_c, ko, ones_o, odt=wa.WA_F32)
+    # probabilities are rounded to bf16 before the value product: |O - 1| <= 2^-8
+    assert np.abs(to_f64(out) - 1.0).max() <= 2.0 ** -8
+    vc, vo = rand_rows(wl, 300, 3), rand_rows(wl, 70, 5)
+    a = attend(wl, q, kc, vc, ko, vo, odt=wa.WA_BF16)
+    b = attend(wl, q, kc, vc, ko, vo, odt=wa.WA_BF16)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_attention_invariant_to_page_order():
+    """Permuting the pages of the gathered context changes nothing beyond
+    rounding (one softmax over the whole set)."""
+    wl = BF
+    pages_k = [rand_rows(wl, 64, 10 + j) for j in range(4)]
+    pages_v = [rand_rows(wl, 64, 20 + j) for j in range(4)]
+    q, ko, vo = rand_rows(wl, 80, 1), rand_rows(wl, 80, 2), rand_rows(wl, 80, 3)
+    a = attend(wl, q, np.concatenate(pages_k), np.concatenate(pages_v), ko, vo, odt=wa.WA_F32)
+    order = [3, 1, 0, 2]
+    b = attend(wl, q, np.concatenate([pages_k[i] for i in order]),
+               np.concatenate([pages_v[i] for i in order]), ko, vo, odt=wa.WA_F32)
+    assert np.abs(to_f64(a) - to_f64(b)).max() <= 1e-2
+
+
+def test_append_mean_only_and_rerun():
+    wl = BF
+    run = PoolRun(wl)
+    k, v = W.page_kv(wl, 2)
+    # producer wrote the page in place: k_src is the slot itself
+    run.k_pool[1].copy_(to_device(k))
+    say("append mean-only")
+    wa.wa_append_page(run.L, run.k_pool[1], None, run.k_pool, None, 1, run.means,
+                      workspace=run.ws)
+    torch.cuda.synchronize()
+    want = oracle.page_mean(k)
+    got = run.means[1].cpu().numpy()
+    assert np.abs(got - want).max() <= 1e-12
+    # the V slot was not touched, the K slot still holds the page
+    assert torch.count_nonzero(run.v_pool[1]).item() == 0
+    assert to_bits(run.k_pool[1]).tobytes() == k.tobytes()
+    first = run.means[1].clone()
+    wa.wa_append_page(run.L, run.k_pool[1], None, run.k_pool, None, 1, run.means,
+                      workspace=run.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, run.means[1])
+
+
+def _pool_with_pages(wl, n):
+    run = PoolRun(wl)
+    for j in range(n):
+        run.append(j)
+    return run
+
+
+def test_select_with_explicit_candidates_and_all_pages():
+    wl = BF
+    run = _pool_with_pages(wl, wl.n_pages)
+    q = W.chunk_qkv(wl, 0, 0)[0]
+    qd = to_device(q)
+    host_means = run.oracle_means(range(wl.n_pages))
+    for cand, k_p in (([4, 1, 3], 2), ([2, 0, 4, 1, 3], 5), ([3], 1)):
+        cd = torch.tensor(cand, dtype=torch.int32, device="cuda")
+        say("select cand", cand, k_p)
+        idx = wa.wa_select_pages(run.L, qd, run.means, k_p, cand=cd)
+        ref = oracle.select_pages(q, host_means, k_p, cand=np.array(cand, np.int32))
+        assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+
+
+def test_select_skips_out_of_range_candidates():
+    wl = BF
+    run = _pool_with_pages(wl, wl.n_pages)
+    q = W.chunk_qkv(wl, 0, 0)[0]
+    cand = [2, 99, -4, 0, 3]
+    cd = torch.tensor(cand, dtype=torch.int32, device="cuda")
+    scores = torch.empty(5, dtype=torch.float64, device="cuda")
+    say("select invalid cand")
+    idx = wa.wa_select_pages(run.L, to_device(q), run.means, 5, cand=cd, out_scores=scores)
+    got = idx.cpu().numpy().tolist()
+    ref = oracle.select_pages(q, run.oracle_means(range(wl.n_pages)), 3,
+                              cand=np.array([2, 0, 3], np.int32))
+    assert got[:3] == ref["idx"].tolist() and got[3:] == [-1, -1]
+    s = scores.cpu().numpy()
+    assert np.isneginf(s[1]) and np.isneginf(s[2])
+
+
+def test_gather_skips_out_of_range_index():
+    wl = BF
+    run = _pool_with_pages(wl, wl.n_pages)
+    idx = torch.tensor([3, 7, -1, 0], dtype=torch.int32, device="cuda")
+    shape = (4 * wl.page_tokens, wl.n_heads, wl.head_dim)
+    k_ctx = torch.full(shape, 5.0, dtype=torch.bfloat16, device="cuda")
+    v_ctx = torch.full(shape, 5.0, dtype=torch.bfloat16, device="cuda")
+    say("gather invalid idx")
+    wa.wa_gather(run.L, run.k_pool, run.v_pool, idx, 4, k_ctx, v_ctx)
+    torch.cuda.synchronize()
+    pt = wl.page_tokens
+    assert to_bits(k_ctx[:pt]).tobytes() == run.host_k[3].tobytes()
+    assert to_bits(v_ctx[3 * pt:]).tobytes() == run.host_v[0].tobytes()
+    assert bool((k_ctx[pt:3 * pt] == 5.0).all()) and bool((v_ctx[pt:3 * pt] == 5.0).all())
+
+
+def test_selection_follows_pool_slots_under_permutation():
+    """Pages stored in permuted slots: the selected slots map back to the same
+    pages, and the gathered buffers are identical."""
+    wl = BF
+    perm = [3, 0, 4, 1, 2]            # page j lives in slot perm[j]
+    a = PoolRun(wl)
+    b = PoolRun(wl)
+    for j in range(wl.n_pages):
+        a.append(j)
+        b.append(j, slot=perm[j])
+    qd = to_device(W.chunk_qkv(wl, 0, 0)[0])
+    ia = wa.wa_select_pages(a.L, qd, a.means, wl.k_p).cpu().numpy()
+    ib = wa.wa_select_pages(b.L, qd, b.means, wl.k_p).cpu().numpy()
+    inv = {s: j for j, s in enumerate(perm)}
+    # ties impossible here (distinct offsets); same pages in the same rank order
+    assert [inv[s] for s in ib.tolist()] == ia.tolist()
+    ka, va = wa.wa_gather(a.L, a.k_pool, a.v_pool, torch.from_numpy(ia).cuda(), wl.k_p)
+    kb, vb = wa.wa_gather(b.L, b.k_pool, b.v_pool, torch.from_numpy(ib).cuda(), wl.k_p)
+    assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
+    assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
