@@ -1,0 +1,257 @@
+"""Benchmark of the paged-KV block-attention path on one MI355X.
+
+Workload: the Wan2.1-1.3B-shaped layer -- 12 heads of dimension 128, pages of
+8 frames x 1,560 tokens (12,480 tokens), 16 resident pages, a 3-frame chunk
+(4,680 queries and 4,680 own K/V tokens), K_p = 4, so 49,920 gathered + 4,680
+own keys per head; bf16 inputs, one denoising step per chunk.
+
+One step = one pass of the whole path over the chunk, on one stream:
+  append the chunk's page (copy into a spare pool slot + fp64 mean key),
+  select (mean query -> scores over the 16 pages -> top-4),
+  gather the 4 pages into one contiguous K/V buffer,
+  block attention of the 4,680 queries over 54,600 keys.
+Inputs are resident in HBM before the timed region.
+
+Output: one JSON line.  `value` is block-attention TFLOP/s over the whole
+step (attention FLOPs / step time).  Kernel-level figures (attention TFLOP/s
+and its fraction of the bf16 matrix-core peak, select + gather GB/s and its
+fraction of HBM peak) are measured with HIP events on the launch stream.
+The CPU baseline is the fp64 oracle timed on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def attention_flops(n_q, n_k, head_dim, n_heads):
+    """2 FLOP per multiply-add, two contractions (Q K^T and P V); softmax excluded."""
+    return 4.0 * n_q * n_k * head_dim * n_heads
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle sample for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attention_wan_kp4_traffic.json"),
+                    help="HBM traffic summary from rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the path is built and measured on one GPU's "
+              "share (see the sharding note in DESIGN.md); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_attention_page_amd as wa
+    import wa_workloads as W
+
+    wl = W.WORKLOADS["wan_kp4"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L = wa.layout(wa.WA_BF16, wl.n_heads, wl.head_dim, wl.page_tokens, wl.n_pages + 1)
+    spare = wl.n_pages                     # slot the per-step append writes
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs, resident in HBM before timing
+    shape = (L.max_pages, wl.page_tokens, wl.n_heads, wl.head_dim)
+    k_pool = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    means = torch.zeros(L.max_pages, wl.n_heads, wl.head_dim, dtype=torch.float64, device=dev)
+    ws_append = torch.empty(wa.wa_append_workspace_bytes(L), dtype=torch.uint8, device=dev)
+    for j in range(wl.n_pages):
+        k, v = W.page_kv(wl, j)
+        k_pool[j].copy_(up(k))
+        v_pool[j].copy_(up(v))
+    for j in range(wl.n_pages):
+        wa.wa_append_page(L, k_pool[j], v_pool[j], k_pool, v_pool, j, means, workspace=ws_append)
+    k_new, v_new = W.page_kv(W.scaled(wl, n_pages=wl.n_pages + 1), wl.n_pages)
+    k_new, v_new = up(k_new), up(v_new)
+    q_h, ko_h, vo_h = W.chunk_qkv(wl, 0, 0)
+    q, k_own, v_own = up(q_h), up(ko_h), up(vo_h)
+    cand = torch.arange(wl.n_pages, dtype=torch.int32, device=dev)
+    idx = torch.empty(wl.k_p, dtype=torch.int32, device=dev)
+    ws_sel = torch.empty(wa.wa_select_workspace_bytes(L, wl.n_q, wl.n_pages), dtype=torch.uint8,
+                         device=dev)
+    ctx_shape = (wl.n_ctx, wl.n_heads, wl.head_dim)
+    k_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
+    v_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
+    out = torch.empty((wl.n_q, wl.n_heads, wl.head_dim), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    n_k = wl.n_ctx + wl.n_q
+    flops = attention_flops(wl.n_q, n_k, wl.head_dim, wl.n_heads)
+    page_bytes = wl.page_tokens * wl.n_heads * wl.head_dim * 2
+    row_means = wl.n_heads * wl.head_dim * 8
+    bytes_append = 2 * 2 * page_bytes + row_means
+    bytes_select = wl.n_q * wl.n_heads * wl.head_dim * 2 + wl.n_pages * row_means + 4 * wl.k_p
+    bytes_gather = 2 * 2 * wl.k_p * page_bytes
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def step(timed=None):
+        if timed is not None:
+            timed[0].record(stream)
+        wa.wa_append_page(L, k_new, v_new, k_pool, v_pool, spare, means, workspace=ws_append,
+                          stream=stream)
+        if timed is not None:
+            timed[1].record(stream)
+        wa.wa_select_pages(L, q, means, wl.k_p, cand=cand, out_idx=idx, workspace=ws_sel,
+                           stream=stream)
+        if timed is not None:
+            timed[2].record(stream)
+        wa.wa_gather(L, k_pool, v_pool, idx, wl.k_p, k_ctx, v_ctx, stream=stream)
+        if timed is not None:
+            timed[3].record(stream)
+        wa.wa_block_attention(L, q, k_ctx, v_ctx, k_own, v_own, wl.softmax_scale,
+                              out_dtype=wa.WA_BF16, out=out, stream=stream)
+        if timed is not None:
+            timed[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing: K steps between two synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel timing: HIP events on the launch stream around each call
+    per = {"append": [], "select": [], "gather": [], "attention": []}
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        step(evs)
+        torch.cuda.synchronize()
+        per["append"].append(evs[0].elapsed_time(evs[1]))
+        per["select"].append(evs[1].elapsed_time(evs[2]))
+        per["gather"].append(evs[2].elapsed_time(evs[3]))
+        per["attention"].append(evs[3].elapsed_time(evs[4]))
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    med = {k: float(np.median(v)) for k, v in per.items()}
+
+    attn_tflops = flops / (avg["attention"] * 1e-3) / 1e12
+    sg_gbps = (bytes_select + bytes_gather) / ((avg["select"] + avg["gather"]) * 1e-3) / 1e9
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            t = json.load(f)
+        traffic = t.get("bytes_per_launch")
+
+    result = {
+        "metric": "block-attn TFLOP/s (MFMA %) + select/gather HBM GB/s at Kp=4, 49,920-tok KV",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "wan_kp4: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, "
+                        "16 resident pages, K_p=4, 4,680-query chunk, 49,920+4,680 keys, "
+                        "1 denoising step",
+            "n_heads": wl.n_heads, "head_dim": wl.head_dim, "page_tokens": wl.page_tokens,
+            "pages": wl.n_pages, "k_p": wl.k_p, "n_q": wl.n_q, "n_ctx": wl.n_ctx,
+            "n_keys": n_k, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_attn_bf16",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernels_ms": {k: round(v, 4) for k, v in avg.items()},
+        "kernels_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "select_gather": {
+            "bytes": bytes_select + bytes_gather,
+            "GB/s": round(sg_gbps, 1),
+            "hbm_frac": round(sg_gbps / PEAK_HBM_GBPS, 4),
+            "gather_GB/s": round(bytes_gather / (avg["gather"] * 1e-3) / 1e9, 1),
+            "select_GB/s": round(bytes_select / (avg["select"] * 1e-3) / 1e9, 1),
+        },
+        "append": {
+            "bytes": bytes_append,
+            "GB/s": round(bytes_append / (avg["append"] * 1e-3) / 1e9, 1),
+        },
+        "flops_per_step": flops,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h,
+                                              args.cpu_seconds, torch)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, seconds, torch):
+    """The fp64 oracle's attention on a bounded sample of query rows (all heads),
+    on the host cores, in the metric's unit (TFLOP/s)."""
+    import oracle
+    oracle.build(force=False)
+    sel = idx.cpu().numpy()
+    k_ctx = np.ascontiguousarray(k_pool[torch.from_numpy(sel).long()].view(torch.uint16).cpu()
+                                 .numpy().reshape(-1, wl.n_heads, wl.head_dim))
+    v_ctx = np.ascontiguousarray(v_pool[torch.from_numpy(sel).long()].view(torch.uint16).cpu()
+                                 .numpy().reshape(-1, wl.n_heads, wl.head_dim))
+    n_k = k_ctx.shape[0] + ko_h.shape[0]
+    threads = oracle.n_threads()
+    rows = np.arange(0, wl.n_q, wl.n_q // 8, dtype=np.int64)[:8]
+    t0 = time.perf_counter()
+    oracle.attention(q_h, k_ctx, v_ctx, ko_h, vo_h, wl.softmax_scale, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    n_rows = int(min(wl.n_q, max(8, round(8 * seconds / max(dt, 1e-3)))))
+    if n_rows > 8:
+        rows = np.unique(np.linspace(0, wl.n_q - 1, n_rows).round().astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.attention(q_h, k_ctx, v_ctx, ko_h, vo_h, wl.softmax_scale, rows=rows,
+                         threads=threads)
+        dt = time.perf_counter() - t0
+    fl = attention_flops(len(rows), n_k, wl.head_dim, wl.n_heads)
+    return {
+        "value": round(fl / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "block attention of %d of %d query rows x %d heads over %d keys (fp64, "
+                  "%.1f s)" % (len(rows), wl.n_q, wl.n_heads, n_k, dt),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -89,7 +89,8 @@ def _dtype_code(x: np.ndarray) -> int:
 
 
 def n_threads() -> int:
-    return max(1, os.cpu_count() or 1)
+    """Threads for the attention loop: the host's cores, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 # ----------------------------------------------------------------------------
