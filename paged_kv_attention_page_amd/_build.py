@@ -20,6 +20,13 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
              "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 
 
+# Per-source flags.  The attention kernel asks for the VGPR form of the
+# matrix-core instructions: its score tiles feed vector ALU work directly, and
+# the long-lived query fragments and output accumulators are pinned to AGPRs
+# in the source.
+EXTRA_FLAGS = {"k_attn_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -34,7 +41,8 @@ def sources() -> list[str]:
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + HIP_FLAGS + lang + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + HIP_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + lang + \
+        ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))

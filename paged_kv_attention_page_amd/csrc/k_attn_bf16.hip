@@ -24,10 +24,11 @@
 //    row-major V tile into the key-contiguous operand, in the key order that
 //    matches P.
 //  * Software pipeline per wave: the Q K^T products of the next sub-tile are
-//    issued before the exponentials of the current one, so matrix-core and
-//    vector work overlap; the output is only rescaled when a query's max
-//    grows by more than 2^8 in the exp2 domain (exact either way: the final
-//    division uses the same reference max).
+//    interleaved with the exponentials of the current one, and the P V
+//    products with the next sub-tile's max (sched_group_barrier patterns), so
+//    matrix-core and vector work overlap; the output is only rescaled when a
+//    query's max grows by more than 2^8 in the exp2 domain (exact either way:
+//    the final division uses the same reference max).
 #include <math.h>
 
 #include "wa_internal.h"
@@ -77,8 +78,32 @@ __device__ __forceinline__ void dma16(const void *gptr, unsigned lds_base) {
                  : "s"(lds_base), "v"(gptr)
                  : "memory", "m0");
 }
+// The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset: the per-lane offsets of a tile never change, so issuing a tile
+// costs no vector instructions beyond the copies themselves.
+__device__ __forceinline__ void dma16_sbase(const void *sbase, unsigned voff, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+
+// Pin a value at this point of the instruction stream: it must be computed
+// before here and may not sink below.  Used with sched_barrier(0) to lay out
+// the matrix-core / vector interleave of the fused regions explicitly.
+template <typename T>
+__device__ __forceinline__ void pin(T &v) {
+    asm volatile("" : "+v"(v));
+}
+// Ask for a value to live in accumulation registers (AGPRs): the matrix cores
+// read their operands and accumulators from there, and it leaves the vector
+// registers to the softmax.
+template <typename T>
+__device__ __forceinline__ void pin_acc(T &v) {
+    asm volatile("" : "+a"(v));
+}
 
 __device__ __forceinline__ unsigned lds_addr(const void *p) {
     return (unsigned)(uintptr_t)(const WA_LDS void *)p;
@@ -142,8 +167,37 @@ void k_attn_bf16(AttnArgs a) {
     const int ld_row0 = 16 * wave + (lane >> 4);
     const int ld_slot = lane & 15;
     const unsigned ld_base = __builtin_amdgcn_readfirstlane(16 * wave * kD * 2);
+    // per-lane byte offsets of this lane's 16 bytes within a tile whose first
+    // row is at a uniform base (fast path: the tile lies inside one segment)
+    unsigned koff[4], voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = ld_row0 + 4 * i;
+        const unsigned rowb = (unsigned)(row * hd + h * kD) * 2u;
+        koff[i] = rowb + 16u * (unsigned)(ld_slot ^ (row & 15));
+        voff[i] = rowb + 16u * (unsigned)(ld_slot ^ (4 * (row & 3)));
+    }
     auto issue_tile = [&](int t, uint16_t *ks, uint16_t *vs) __attribute__((always_inline)) {
         const int key0 = t * kBN;
+        const unsigned lk = lds_addr(ks) + ld_base, lv = lds_addr(vs) + ld_base;
+        const uint16_t *kb = nullptr, *vb = nullptr;
+        if (key0 + kBN <= a.n_ctx) {
+            kb = a.k_ctx + (int64_t)key0 * hd;
+            vb = a.v_ctx + (int64_t)key0 * hd;
+        } else if (key0 >= a.n_ctx && key0 + kBN <= n_keys) {
+            kb = a.k_own + (int64_t)(key0 - a.n_ctx) * hd;
+            vb = a.v_own + (int64_t)(key0 - a.n_ctx) * hd;
+        }
+        if (kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dma16_sbase(kb, koff[i], lk + 4 * i * kD * 2);
+                dma16_sbase(vb, voff[i], lv + 4 * i * kD * 2);
+            }
+            return;
+        }
+        // tile across the ctx/own boundary or past the end: per-lane rows
+        asm volatile("; dma slow path" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = ld_row0 + 4 * i;
@@ -153,10 +207,8 @@ void k_attn_bf16(AttnArgs a) {
             const int64_t off = (int64_t)(in_ctx ? n : n - a.n_ctx) * hd + h * kD;
             const uint16_t *kr = (in_ctx ? a.k_ctx : a.k_own) + off;
             const uint16_t *vr = (in_ctx ? a.v_ctx : a.v_own) + off;
-            const int kchunk = ld_slot ^ (row & 15);
-            const int vchunk = ld_slot ^ (4 * (row & 3));
-            dma16(kr + 8 * kchunk, lds_addr(ks) + ld_base + 4 * i * kD * 2);
-            dma16(vr + 8 * vchunk, lds_addr(vs) + ld_base + 4 * i * kD * 2);
+            dma16(kr + 8 * (ld_slot ^ (row & 15)), lk + 4 * i * kD * 2);
+            dma16(vr + 8 * (ld_slot ^ (4 * (row & 3))), lv + 4 * i * kD * 2);
         }
     };
 
@@ -174,56 +226,78 @@ void k_attn_bf16(AttnArgs a) {
         }
     }
 
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int st = 0; st < 8; ++st) pin_acc(qf[qb][st]);
+
     f32x16 o[4][2];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[b][qb][i] = 0.f;
+            pin_acc(o[b][qb]);
+        }
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-    // ---- S^T of 32 keys (sub-tile `sub` of tile stage `stage`) against the 64 queries
-    // per-lane byte offsets of the K operand reads (one per 16-wide d step)
+    // ---- per-lane byte offsets of the operand reads
+    // K (A operand of S^T = K Q^T): row lr of the 32-key sub-tile, d chunk 2st+hb
     int kofs[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) kofs[st] = 2 * (lr * kD + (((2 * st + hb) ^ (lr & 15)) << 3));
-    auto qk = [&](const uint16_t *kt, int sub, f32x16 (&s)[2]) __attribute__((always_inline)) {
-        const WA_LDS char *kb = (const WA_LDS char *)kt + sub * 32 * kD * 2;
+    // V^T (A operand of O^T += V^T P^T) for dv block b: lane group g = lane/16
+    // supplies keys 4hb + u/4 (+16jj, +8 for the upper half of the 16 keys) and
+    // dims 32b + 16(g&1) + 4(u%4) .. +3 of the row-major tile; the transpose
+    // read hands lane 16g+i dim 32b+16(g&1)+i over those keys, in the key order
+    // of the S^T accumulator (keys 8(i/4) + 4hb + i%4 of each 16-key step).
+    int vofs[4];
+    {
+        const int u = lane & 15, g = lane >> 4;
+        const int r = 4 * hb + (u >> 2);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[qb][i] = 0.f;
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const bf16x8 ak = *(const WA_LDS bf16x8 *)(kb + kofs[st]);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[0][st], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[1][st], s[1], 0, 0, 0);
+        for (int b = 0; b < 4; ++b) {
+            const int cidx = 4 * b + 2 * (g & 1) + ((u & 3) >> 1);
+            vofs[b] = r * (kD * 2) + ((cidx ^ (4 * (r & 3))) << 4) + 8 * (u & 1);
         }
+    }
+    auto read_k = [&](const uint16_t *kt, int sub, int st) __attribute__((always_inline)) -> bf16x8 {
+        return *(const WA_LDS bf16x8 *)((const WA_LDS char *)kt + sub * 32 * kD * 2 + kofs[st]);
+    };
+    // V^T operand `op` = 4 jj + b of sub-tile `sub`
+    auto read_v = [&](const uint16_t *vt, int sub, int op) __attribute__((always_inline)) -> bf16x8 {
+        const int jj = op >> 2, b = op & 3;
+        const WA_LDS char *base = (const WA_LDS char *)vt + (sub * 32 + 16 * jj) * kD * 2 + vofs[b];
+        i16x4 half[2];
+        half[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)base);
+        half[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)(base + 8 * kD * 2));
+        bf16x8 av;
+        __builtin_memcpy(&av, half, sizeof(av));
+        return av;
     };
 
-    // ---- running max of one sub-tile; rescale the output when it grew enough
-    auto row_max = [&](f32x16 (&s)[2], int key0, bool masked) __attribute__((always_inline)) {
-        if (masked) {
+    // ---- keys past the end (last tile only) get score -inf.  Their rows were
+    // loaded as copies of the last key, so maxima taken before masking are
+    // still maxima over real keys; masking only has to precede the exponentials.
+    auto mask_tail = [&](f32x16 (&s)[2], int key0) __attribute__((always_inline)) {
+        asm volatile("; mask tail" ::: "memory");
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 8 * (i >> 2) + 4 * hb + (i & 3);
-                if (key >= n_keys) {
-                    s[0][i] = -INFINITY;
-                    s[1][i] = -INFINITY;
-                }
+        for (int i = 0; i < 16; ++i) {
+            const int key = key0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+            if (key >= n_keys) {
+                s[0][i] = -INFINITY;
+                s[1][i] = -INFINITY;
             }
         }
-        float mt[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float x = s[qb][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) x = fmaxf(x, s[qb][i]);
-            mt[qb] = xhalf_max(x);
-        }
-        const bool grow = mt[0] > m[0] + thr || mt[1] > m[1] + thr;
+    };
+    // ---- move the reference max (and rescale the output) when it grew enough
+    auto rescale = [&](const float (&mt)[2], bool live) __attribute__((always_inline)) {
+        const bool grow = live && (mt[0] > m[0] + thr || mt[1] > m[1] + thr);
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            // a real branch: without this marker the compiler flattens it and
+            // rescales the whole output on every sub-tile
+            asm volatile("; rescale" ::: "memory");
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const float mn = fmaxf(m[qb], mt[qb]);
@@ -238,61 +312,66 @@ void k_attn_bf16(AttnArgs a) {
         }
     };
 
-    // ---- P = exp2(S c - m c) as bf16 B operands; l accumulates the bf16 values
-    auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+    // ---- fused region QK+SOFTMAX: sn = K(kt, sub) Q^T (16 MFMAs) interleaved
+    // with the exponentials of sc (2 elements of one query block per MFMA),
+    // P packed to bf16 for the P V products, l accumulated from the bf16 values.
+    // ak[0], ak[1] arrive prefetched; the V^T operands 0 and 1 of the following
+    // P V region (sub-tile vsub of vt) are prefetched at the end.
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    auto qk_softmax = [&](const uint16_t *kt, int sub, f32x16 (&sn)[2], const f32x16 (&sc)[2],
+                          bf16x8 (&pb)[2][2], bf16x8 (&ak)[8], const uint16_t *vt, int vsub,
+                          bf16x8 (&av)[8]) __attribute__((always_inline)) {
+        const float mc[2] = {m[0] * c, m[1] * c};
+        float ls[2] = {l[0], l[1]};
+        const f32x16 zero = {};
+        const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float mc = m[qb] * c;
+        for (int st = 0; st < 8; ++st) {
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    pb[qb][jj][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * jj + t], c, -mc));
-            float ls = l[qb];
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (int t = 0; t < 8; t += 2) {
-                    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                    const bf16x2 pair = {pb[qb][jj][t], pb[qb][jj][t + 1]};
-                    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
-                    ls = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls, false);
-                }
-            l[qb] = ls;
-        }
-    };
-
-    // ---- O^T += V^T P^T for sub-tile `sub`.  V^T operand of dv block b, k-step
-    // jj: lane group g = lane/16 supplies keys 4hb + u/4 (+16jj, +8 for the
-    // upper half) and dims 32b + 16(g&1) + 4(u%4) .. +3 of the row-major tile;
-    // the transpose read hands lane 16g+i dims 32b+16(g&1)+i over those keys.
-    int vofs[4];
-    {
-        const int u = lane & 15, g = lane >> 4;
-        const int r = 4 * hb + (u >> 2);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int cidx = 4 * b + 2 * (g & 1) + ((u & 3) >> 1);
-            vofs[b] = r * (kD * 2) + ((cidx ^ (4 * (r & 3))) << 4) + 8 * (u & 1);
-        }
-    }
-    auto pv = [&](const uint16_t *vtile, int sub, const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
-        const WA_LDS char *vt = (const WA_LDS char *)vtile + sub * 32 * kD * 2;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                i16x4 half[2];
-#pragma unroll
-                for (int th = 0; th < 2; ++th)
-                    half[th] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (WA_LDS i16x4 *)(vt + (16 * jj + 8 * th) * kD * 2 + vofs[b]));
-                bf16x8 av;
-                __builtin_memcpy(&av, half, sizeof(av));
-                o[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[0][jj], o[b][0], 0, 0, 0);
-                o[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[1][jj], o[b][1], 0, 0, 0);
+            for (int qb = 0; qb < 2; ++qb) {
+                sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[qb][st],
+                                                                 st == 0 ? zero : sn[qb], 0, 0, 0);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * st], c, -mc[qb]));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * st + 1], c, -mc[qb]));
+                const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
+                pb[qb][st >> 2][2 * (st & 3)] = pr[0];
+                pb[qb][st >> 2][2 * (st & 3) + 1] = pr[1];
+                ls[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls[qb], false);
+                pin(ls[qb]);
+                if (qb == 0 && st + 2 < 8) ak[st + 2] = read_k(kt, sub, st + 2);
+                if (qb == 1 && st >= 6) av[st - 6] = read_v(vt, vsub, st - 6);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        l[0] = ls[0];
+        l[1] = ls[1];
+    };
+
+    // ---- fused region PV+MAX: O^T += V^T P^T (16 MFMAs) interleaved with the
+    // max of sn per query; prefetches the next V^T operands two steps ahead and,
+    // at the end, the first two K operands of the next QK+SOFTMAX region.
+    auto pv_max = [&](const uint16_t *vt, int sub, const bf16x8 (&pb)[2][2], bf16x8 (&av)[8],
+                      const f32x16 (&sn)[2], float (&mt)[2], const uint16_t *kt_next,
+                      int ksub_next, bf16x8 (&ak)[8]) __attribute__((always_inline)) {
+        float x[2] = {fmaxf(sn[0][0], sn[0][1]), fmaxf(sn[1][0], sn[1][1])};
+#pragma unroll
+        for (int op = 0; op < 8; ++op) {
+            const int jj = op >> 2, b = op & 3;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                o[b][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[op], pb[qb][jj], o[b][qb], 0, 0, 0);
+                // 14 remaining values per query block, two per step
+                if (op < 7) {
+                    x[qb] = fmaxf(x[qb], fmaxf(sn[qb][2 + 2 * op], sn[qb][3 + 2 * op]));
+                    pin(x[qb]);
+                }
+                if (qb == 0 && op + 2 < 8) av[op + 2] = read_v(vt, sub, op + 2);
+                if (qb == 1 && op >= 6) ak[op - 6] = read_k(kt_next, ksub_next, op - 6);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        mt[0] = xhalf_max(x[0]);
+        mt[1] = xhalf_max(x[1]);
     };
 
     // ---- prologue: tiles 0 and 1 in flight, wait for tile 0
@@ -307,37 +386,61 @@ void k_attn_bf16(AttnArgs a) {
 
     f32x16 sa[2], sb[2];
     bf16x8 pa[2][2], pbk[2][2];
-    qk(kst<0>(), 0, sa);
+    bf16x8 ak[8], av[8];
+    float mta[2], mtb[2];
+    {
+        // S(0, 0) and its max
+#pragma unroll
+        for (int st = 0; st < 8; ++st) ak[st] = read_k(kst<0>(), 0, st);
+        const f32x16 zero = {};
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[qb][st],
+                                                                 st == 0 ? zero : sa[qb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float x = sa[qb][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[qb][i]);
+            mta[qb] = xhalf_max(x);
+        }
+        rescale(mta, true);
+        if (ragged && n_tiles == 1) mask_tail(sa, 0);
+        ak[0] = read_k(kst<0>(), 1, 0);
+        ak[1] = read_k(kst<0>(), 1, 1);
+    }
 
-    // One tile; stage S holds tile t, stage S+1 tile t+1, stage S+2 is refilled
-    // with tile t+2.  Returns false after the last tile.
+    // Tile t in stage S; on entry sa = S(t, 0) with the reference max already
+    // moved, and the first two K operands of S(t, 1) prefetched.  Stage S+1
+    // holds tile t+1, stage S+2 is refilled with tile t+2.  On exit sa =
+    // S(t+1, 0), likewise.  The last tile runs the same code: its products of
+    // the (nonexistent) next tile read a stale stage and are discarded, which
+    // keeps every fused region one basic block.
     auto tile = [&](int t, auto stage_tag) __attribute__((always_inline)) -> bool {
         constexpr int S = decltype(stage_tag)::value;
         constexpr int S1 = (S + 1) % kStages, S2 = (S + 2) % kStages;
         const bool last = t == n_tiles - 1;
-        const bool mask = ragged && last;
-        // sub-tile 0 softmax, overlapped with the sub-tile 1 products
-        row_max(sa, t * kBN, mask);
-        qk(kst<S>(), 1, sb);
-        softmax(sa, pa);
-        pv(vst<S>(), 0, pa);
-        row_max(sb, t * kBN + 32, mask);
-        if (!last) {
-            // tile t+1 (the only load in flight) must be in LDS for every wave;
-            // every wave is past its reads of tile t-1, whose stage is refilled
-            wait_vm0();
-            __syncthreads();
-            if (t + 2 < n_tiles) issue_tile(t + 2, kst<S2>(), vst<S2>());
-            qk(kst<S1>(), 0, sa);
-        }
-        softmax(sb, pbk);
-        pv(vst<S>(), 1, pbk);
-        return !last;
+        qk_softmax(kst<S>(), 1, sb, sa, pa, ak, vst<S>(), 0, av);
+        // tile t+1 (the only load in flight) must be in LDS for every wave, and
+        // every wave is past its reads of tile t-1, whose stage is refilled
+        wait_vm0();
+        __syncthreads();
+        if (t + 2 < n_tiles) issue_tile(t + 2, kst<S2>(), vst<S2>());
+        pv_max(vst<S>(), 0, pa, av, sb, mtb, kst<S1>(), 0, ak);
+        rescale(mtb, true);
+        if (ragged && last) mask_tail(sb, t * kBN + 32);
+        qk_softmax(kst<S1>(), 0, sa, sb, pbk, ak, vst<S>(), 1, av);
+        pv_max(vst<S>(), 1, pbk, av, sa, mta, kst<S1>(), 1, ak);
+        rescale(mta, !last);
+        if (ragged && t + 1 == n_tiles - 1) mask_tail(sa, (t + 1) * kBN);
+        return last;
     };
     for (int t = 0;; t += 3) {
-        if (!tile(t, StageTag<0>{})) break;
-        if (!tile(t + 1, StageTag<1>{})) break;
-        if (!tile(t + 2, StageTag<2>{})) break;
+        if (tile(t, StageTag<0>{})) break;
+        if (tile(t + 1, StageTag<1>{})) break;
+        if (tile(t + 2, StageTag<2>{})) break;
     }
 
     // ---- epilogue: O^T[dv][q] / l; lanes l and l^32 hold halves of l
