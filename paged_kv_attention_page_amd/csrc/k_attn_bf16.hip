@@ -5,19 +5,22 @@
 // the only contractions, softmax sits between them).
 //
 // Design (gfx950, head_dim 128):
-//  * Block = 4 wavefronts x 64 queries = 256 queries of one head.  Blocks are
-//    renumbered so that consecutive (head, query-block) tiles land on the
-//    same XCD: the blocks of one head then stream the same K/V through one
-//    L2.
+//  * Block = 8 wavefronts x 32 queries = 256 queries of one head, two
+//    wavefronts per SIMD: one wavefront's matrix-core work overlaps the
+//    other's softmax (a single wavefront issues a vector instruction only
+//    every ~8 cycles, too slow to hide the exponentials behind its own
+//    products).  Blocks are renumbered so that consecutive (head, query-block)
+//    tiles land on the same XCD: the blocks of one head then stream the same
+//    K/V through one L2.
 //  * K/V tiles of 64 keys go from global memory straight into LDS with
 //    global_load_lds_dwordx4 (no register staging), in a ring of kStages
 //    tiles; the loads of tile t+kStages-1 are in flight while tile t is
 //    computed.  Both tiles are row-major [key][d] with XOR-swizzled 16-byte
 //    chunks; the swizzle is applied on the global side of the copy.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32 accumulation) on 32-key
-//    sub-tiles: a lane then holds 16 keys of ONE query per query block, so a
-//    query's running max / sum live in one lane pair (one permlane32 swap)
-//    and rescaling the output is a per-lane multiply.
+//    sub-tiles: a lane then holds 16 keys of ONE query, so a query's running
+//    max / sum live in one lane pair (one permlane32 swap) and rescaling the
+//    output is a per-lane multiply.
 //  * O^T += V^T P^T: P comes straight from the S^T accumulator layout
 //    (exp2 of S * scale*log2(e) - m, rounded to bf16); V^T operands are read
 //    with ds_read_b64_tr_b16, whose 16-lane 4x16 -> 16x4 transpose turns the
@@ -36,16 +39,21 @@
 namespace wa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define WA_LDS __attribute__((address_space(3)))
 
-static constexpr int kD = 128;        // head dim
-static constexpr int kBM = 256;       // queries per block
-static constexpr int kBN = 64;        // keys per tile
-static constexpr int kThreads = 256;  // 4 wavefronts
-static constexpr int kStages = 3;     // LDS ring depth (tiles)
+static constexpr int kD = 128;            // head dim
+static constexpr int kWaves = 8;          // wavefronts per block
+static constexpr int kWQ = 32;            // queries per wavefront
+static constexpr int kBM = kWaves * kWQ;  // queries per block
+static constexpr int kBN = 64;            // keys per tile
+static constexpr int kThreads = 64 * kWaves;
+static constexpr int kStages = 4;         // LDS ring depth (tiles)
 static constexpr int kTileElems = kBN * kD;
+static constexpr int kRowsPerWave = kBN / kWaves;   // tile rows each wavefront copies
+static constexpr int kCopies = kRowsPerWave / 4;    // 1 KB copies per tensor per wavefront
 static constexpr float kRescaleLog2 = 8.f;   // rescale when the max grows by > 2^8
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -88,6 +96,7 @@ __device__ __forceinline__ void dma16_sbase(const void *sbase, unsigned voff, un
                  : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 
 // Pin a value at this point of the instruction stream: it must be computed
@@ -124,9 +133,11 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[kTileElems];
 __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[kTileElems];
 __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[kTileElems];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_k3[kTileElems];
 __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[kTileElems];
 __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[kTileElems];
 __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[kTileElems];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_v3[kTileElems];
 
 template <int S>
 struct StageTag {
@@ -138,23 +149,25 @@ __device__ __forceinline__ uint16_t *kst() {
     static_assert(S >= 0 && S < kStages, "stage");
     if constexpr (S == 0) return lds_k0;
     else if constexpr (S == 1) return lds_k1;
-    else return lds_k2;
+    else if constexpr (S == 2) return lds_k2;
+    else return lds_k3;
 }
 template <int S>
 __device__ __forceinline__ uint16_t *vst() {
     if constexpr (S == 0) return lds_v0;
     else if constexpr (S == 1) return lds_v1;
-    else return lds_v2;
+    else if constexpr (S == 2) return lds_v2;
+    else return lds_v3;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bf16(AttnArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, hb = lane >> 5;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int h = logical / a.q_blocks;
-    const int q0 = (logical % a.q_blocks) * kBM + wave * 64;
+    const int q0 = (logical % a.q_blocks) * kBM + wave * kWQ;
     const int64_t hd = (int64_t)a.n_heads * kD;
     const int n_keys = a.n_ctx + a.n_own;
     const int n_tiles = (n_keys + kBN - 1) / kBN;
@@ -162,16 +175,16 @@ void k_attn_bf16(AttnArgs a) {
     const float c = a.c;
     const float thr = kRescaleLog2 / c;   // raw-score growth that forces a rescale
 
-    // ---- tile loads: wave w copies rows 16w ... 16w+15 of the K and V tiles,
-    // 4 rows (1 KB) per instruction; lane -> (row 16w+4i+lane/16, slot lane%16)
-    const int ld_row0 = 16 * wave + (lane >> 4);
+    // ---- tile loads: wavefront w copies rows 8w ... 8w+7 of the K and V
+    // tiles, 4 rows (1 KB) per instruction; lane -> (row 8w+4i+lane/16, slot lane%16)
+    const int ld_row0 = kRowsPerWave * wave + (lane >> 4);
     const int ld_slot = lane & 15;
-    const unsigned ld_base = __builtin_amdgcn_readfirstlane(16 * wave * kD * 2);
+    const unsigned ld_base = __builtin_amdgcn_readfirstlane(kRowsPerWave * wave * kD * 2);
     // per-lane byte offsets of this lane's 16 bytes within a tile whose first
     // row is at a uniform base (fast path: the tile lies inside one segment)
-    unsigned koff[4], voff[4];
+    unsigned koff[kCopies], voff[kCopies];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kCopies; ++i) {
         const int row = ld_row0 + 4 * i;
         const unsigned rowb = (unsigned)(row * hd + h * kD) * 2u;
         koff[i] = rowb + 16u * (unsigned)(ld_slot ^ (row & 15));
@@ -190,7 +203,7 @@ void k_attn_bf16(AttnArgs a) {
         }
         if (kb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < kCopies; ++i) {
                 dma16_sbase(kb, koff[i], lk + 4 * i * kD * 2);
                 dma16_sbase(vb, voff[i], lv + 4 * i * kD * 2);
             }
@@ -199,7 +212,7 @@ void k_attn_bf16(AttnArgs a) {
         // tile across the ctx/own boundary or past the end: per-lane rows
         asm volatile("; dma slow path" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kCopies; ++i) {
             const int row = ld_row0 + 4 * i;
             int n = key0 + row;
             n = n < n_keys ? n : n_keys - 1;           // rows past the end repeat the last key
@@ -212,35 +225,26 @@ void k_attn_bf16(AttnArgs a) {
         }
     };
 
-    // ---- this wave's 64 queries as B operands: qf[qb][st] = Q[q0+32qb+lr][16st+8hb ..+7]
-    bf16x8 qf[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int row = q0 + 32 * qb + lr;
+    // ---- this wavefront's 32 queries as B operands: qf[st] = Q[q0+lr][16st+8hb ..+7]
+    bf16x8 qf[8];
+    {
+        const int row = q0 + lr;
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
             if (row < a.n_q)
-                qf[qb][st] = *(const bf16x8 *)(a.q + (int64_t)row * hd + h * kD + 16 * st + 8 * hb);
+                qf[st] = *(const bf16x8 *)(a.q + (int64_t)row * hd + h * kD + 16 * st + 8 * hb);
             else
-                qf[qb][st] = (bf16x8)(__bf16)0.f;
+                qf[st] = (bf16x8)(__bf16)0.f;
+            pin_acc(qf[st]);
         }
     }
 
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int st = 0; st < 8; ++st) pin_acc(qf[qb][st]);
-
-    f32x16 o[4][2];
+    f32x16 o[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[b][qb][i] = 0.f;
-            pin_acc(o[b][qb]);
-        }
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+        for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
+    float m = -INFINITY, l = 0.f;
 
     // ---- per-lane byte offsets of the operand reads
     // K (A operand of S^T = K Q^T): row lr of the 32-key sub-tile, d chunk 2st+hb
@@ -280,114 +284,96 @@ void k_attn_bf16(AttnArgs a) {
     // ---- keys past the end (last tile only) get score -inf.  Their rows were
     // loaded as copies of the last key, so maxima taken before masking are
     // still maxima over real keys; masking only has to precede the exponentials.
-    auto mask_tail = [&](f32x16 (&s)[2], int key0) __attribute__((always_inline)) {
+    auto mask_tail = [&](f32x16 &s, int key0) __attribute__((always_inline)) {
         asm volatile("; mask tail" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = key0 + 8 * (i >> 2) + 4 * hb + (i & 3);
-            if (key >= n_keys) {
-                s[0][i] = -INFINITY;
-                s[1][i] = -INFINITY;
-            }
+            if (key >= n_keys) s[i] = -INFINITY;
         }
     };
     // ---- move the reference max (and rescale the output) when it grew enough
-    auto rescale = [&](const float (&mt)[2], bool live) __attribute__((always_inline)) {
-        const bool grow = live && (mt[0] > m[0] + thr || mt[1] > m[1] + thr);
+    auto rescale = [&](float mt, bool live) __attribute__((always_inline)) {
+        const bool grow = live && mt > m + thr;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             // a real branch: without this marker the compiler flattens it and
             // rescales the whole output on every sub-tile
             asm volatile("; rescale" ::: "memory");
+            const float mn = fmaxf(m, mt);
+            const float corr = __builtin_amdgcn_exp2f((m - mn) * c);
+            l *= corr;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float mn = fmaxf(m[qb], mt[qb]);
-                const float corr = __builtin_amdgcn_exp2f((m[qb] - mn) * c);
-                l[qb] *= corr;
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) o[b][qb][i] *= corr;
-                m[qb] = mn;
-            }
+                for (int i = 0; i < 16; ++i) o[b][i] *= corr;
+            m = mn;
         }
     };
 
-    // ---- fused region QK+SOFTMAX: sn = K(kt, sub) Q^T (16 MFMAs) interleaved
-    // with the exponentials of sc (2 elements of one query block per MFMA),
-    // P packed to bf16 for the P V products, l accumulated from the bf16 values.
-    // ak[0], ak[1] arrive prefetched; the V^T operands 0 and 1 of the following
-    // P V region (sub-tile vsub of vt) are prefetched at the end.
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    auto qk_softmax = [&](const uint16_t *kt, int sub, f32x16 (&sn)[2], const f32x16 (&sc)[2],
-                          bf16x8 (&pb)[2][2], bf16x8 (&ak)[8], const uint16_t *vt, int vsub,
+    // ---- fused region QK+SOFTMAX: sn = K(kt, sub) Q^T (8 MFMAs) interleaved
+    // with the exponentials of sc (2 elements per MFMA), P packed to bf16 for
+    // the P V products, l accumulated from the bf16 values.  ak[0], ak[1]
+    // arrive prefetched; the V^T operands 0 and 1 of the following P V region
+    // (sub-tile vsub of vt) are prefetched at the end.
+    auto qk_softmax = [&](const uint16_t *kt, int sub, f32x16 &sn, const f32x16 &sc,
+                          bf16x8 (&pb)[2], bf16x8 (&ak)[8], const uint16_t *vt, int vsub,
                           bf16x8 (&av)[8]) __attribute__((always_inline)) {
-        const float mc[2] = {m[0] * c, m[1] * c};
-        float ls[2] = {l[0], l[1]};
+        const float mc = m * c;
+        float ls = l;
         const f32x16 zero = {};
         const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[qb][st],
-                                                                 st == 0 ? zero : sn[qb], 0, 0, 0);
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * st], c, -mc[qb]));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * st + 1], c, -mc[qb]));
-                const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
-                pb[qb][st >> 2][2 * (st & 3)] = pr[0];
-                pb[qb][st >> 2][2 * (st & 3) + 1] = pr[1];
-                ls[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls[qb], false);
-                pin(ls[qb]);
-                if (qb == 0 && st + 2 < 8) ak[st + 2] = read_k(kt, sub, st + 2);
-                if (qb == 1 && st >= 6) av[st - 6] = read_v(vt, vsub, st - 6);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sn, 0, 0, 0);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st], c, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st + 1], c, -mc));
+            const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
+            pb[st >> 2][2 * (st & 3)] = pr[0];
+            pb[st >> 2][2 * (st & 3) + 1] = pr[1];
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls, false);
+            if (st + 2 < 8) ak[st + 2] = read_k(kt, sub, st + 2);
+            if (st >= 6) av[st - 6] = read_v(vt, vsub, st - 6);
         }
-        l[0] = ls[0];
-        l[1] = ls[1];
+        l = ls;
     };
 
-    // ---- fused region PV+MAX: O^T += V^T P^T (16 MFMAs) interleaved with the
+    // ---- fused region PV+MAX: O^T += V^T P^T (8 MFMAs) interleaved with the
     // max of sn per query; prefetches the next V^T operands two steps ahead and,
     // at the end, the first two K operands of the next QK+SOFTMAX region.
-    auto pv_max = [&](const uint16_t *vt, int sub, const bf16x8 (&pb)[2][2], bf16x8 (&av)[8],
-                      const f32x16 (&sn)[2], float (&mt)[2], const uint16_t *kt_next,
-                      int ksub_next, bf16x8 (&ak)[8]) __attribute__((always_inline)) {
-        float x[2] = {fmaxf(sn[0][0], sn[0][1]), fmaxf(sn[1][0], sn[1][1])};
+    auto pv_max = [&](const uint16_t *vt, int sub, const bf16x8 (&pb)[2], bf16x8 (&av)[8],
+                      const f32x16 &sn, float &mt, const uint16_t *kt_next, int ksub_next,
+                      bf16x8 (&ak)[8]) __attribute__((always_inline)) {
+        float x = fmaxf(sn[0], sn[1]);
 #pragma unroll
         for (int op = 0; op < 8; ++op) {
             const int jj = op >> 2, b = op & 3;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                o[b][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[op], pb[qb][jj], o[b][qb], 0, 0, 0);
-                // 14 remaining values per query block, two per step
-                if (op < 7) {
-                    x[qb] = fmaxf(x[qb], fmaxf(sn[qb][2 + 2 * op], sn[qb][3 + 2 * op]));
-                    pin(x[qb]);
-                }
-                if (qb == 0 && op + 2 < 8) av[op + 2] = read_v(vt, sub, op + 2);
-                if (qb == 1 && op >= 6) ak[op - 6] = read_k(kt_next, ksub_next, op - 6);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[op], pb[jj], o[b], 0, 0, 0);
+            if (op < 7) x = fmaxf(x, fmaxf(sn[2 + 2 * op], sn[3 + 2 * op]));
+            if (op + 2 < 8) av[op + 2] = read_v(vt, sub, op + 2);
+            if (op >= 6) ak[op - 6] = read_k(kt_next, ksub_next, op - 6);
         }
-        mt[0] = xhalf_max(x[0]);
-        mt[1] = xhalf_max(x[1]);
+        mt = xhalf_max(x);
     };
 
-    // ---- prologue: tiles 0 and 1 in flight, wait for tile 0
+    // ---- prologue: tiles 0, 1 and 2 in flight, wait for tile 0
+    static_assert(2 * kCopies == 4, "the waits below count 4 copies per tile");
     issue_tile(0, kst<0>(), vst<0>());
-    if (n_tiles > 1) {
+    if (n_tiles > 2) {
         issue_tile(1, kst<1>(), vst<1>());
+        issue_tile(2, kst<2>(), vst<2>());
         wait_vm8();
+    } else if (n_tiles > 1) {
+        issue_tile(1, kst<1>(), vst<1>());
+        wait_vm4();
     } else {
         wait_vm0();
     }
     __syncthreads();
 
-    f32x16 sa[2], sb[2];
-    bf16x8 pa[2][2], pbk[2][2];
+    f32x16 sa, sb;
+    bf16x8 pa[2], pbk[2];
     bf16x8 ak[8], av[8];
-    float mta[2], mtb[2];
+    float mta, mtb;
     {
         // S(0, 0) and its max
 #pragma unroll
@@ -395,17 +381,11 @@ void k_attn_bf16(AttnArgs a) {
         const f32x16 zero = {};
 #pragma unroll
         for (int st = 0; st < 8; ++st)
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sa, 0, 0, 0);
+        float x = sa[0];
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-                sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[qb][st],
-                                                                 st == 0 ? zero : sa[qb], 0, 0, 0);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float x = sa[qb][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[qb][i]);
-            mta[qb] = xhalf_max(x);
-        }
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[i]);
+        mta = xhalf_max(x);
         rescale(mta, true);
         if (ragged && n_tiles == 1) mask_tail(sa, 0);
         ak[0] = read_k(kst<0>(), 1, 0);
@@ -413,21 +393,25 @@ void k_attn_bf16(AttnArgs a) {
     }
 
     // Tile t in stage S; on entry sa = S(t, 0) with the reference max already
-    // moved, and the first two K operands of S(t, 1) prefetched.  Stage S+1
-    // holds tile t+1, stage S+2 is refilled with tile t+2.  On exit sa =
-    // S(t+1, 0), likewise.  The last tile runs the same code: its products of
+    // moved, and the first two K operands of S(t, 1) prefetched.  Stages S+1
+    // and S+2 hold (or are receiving) tiles t+1 and t+2; stage S+3 is refilled
+    // with tile t+3.  On exit sa = S(t+1, 0), likewise.  The last tile runs the same code: its products of
     // the (nonexistent) next tile read a stale stage and are discarded, which
     // keeps every fused region one basic block.
     auto tile = [&](int t, auto stage_tag) __attribute__((always_inline)) -> bool {
         constexpr int S = decltype(stage_tag)::value;
-        constexpr int S1 = (S + 1) % kStages, S2 = (S + 2) % kStages;
+        constexpr int S1 = (S + 1) % kStages, S3 = (S + 3) % kStages;
         const bool last = t == n_tiles - 1;
         qk_softmax(kst<S>(), 1, sb, sa, pa, ak, vst<S>(), 0, av);
-        // tile t+1 (the only load in flight) must be in LDS for every wave, and
-        // every wave is past its reads of tile t-1, whose stage is refilled
-        wait_vm0();
+        // tile t+1 must be in LDS for every wave (tile t+2 may still be in
+        // flight), and every wave is past its reads of tile t-1, whose stage
+        // is refilled
+        if (t + 2 < n_tiles)
+            wait_vm4();
+        else
+            wait_vm0();
         __syncthreads();
-        if (t + 2 < n_tiles) issue_tile(t + 2, kst<S2>(), vst<S2>());
+        if (t + 3 < n_tiles) issue_tile(t + 3, kst<S3>(), vst<S3>());
         pv_max(vst<S>(), 0, pa, av, sb, mtb, kst<S1>(), 0, ak);
         rescale(mtb, true);
         if (ragged && last) mask_tail(sb, t * kBN + 32);
@@ -437,38 +421,36 @@ void k_attn_bf16(AttnArgs a) {
         if (ragged && t + 1 == n_tiles - 1) mask_tail(sa, (t + 1) * kBN);
         return last;
     };
-    for (int t = 0;; t += 3) {
+    for (int t = 0;; t += 4) {
         if (tile(t, StageTag<0>{})) break;
         if (tile(t + 1, StageTag<1>{})) break;
         if (tile(t + 2, StageTag<2>{})) break;
+        if (tile(t + 3, StageTag<3>{})) break;
     }
 
     // ---- epilogue: O^T[dv][q] / l; lanes l and l^32 hold halves of l
+    const float lt = xhalf_sum(l);
+    const float inv = 1.f / lt;
+    const int row = q0 + lr;
+    if (row < a.n_q) {
+        const int64_t base = (int64_t)row * hd + h * kD;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float lt = xhalf_sum(l[qb]);
-        const float inv = 1.f / lt;
-        const int row = q0 + 32 * qb + lr;
-        if (row < a.n_q) {
-            const int64_t base = (int64_t)row * hd + h * kD;
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int dv = 32 * b + 8 * g + 4 * hb;
-                    const float x0 = o[b][qb][4 * g] * inv, x1 = o[b][qb][4 * g + 1] * inv;
-                    const float x2 = o[b][qb][4 * g + 2] * inv, x3 = o[b][qb][4 * g + 3] * inv;
-                    if (a.out_bf16) {
-                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                        bf16x4 v = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
-                        *(bf16x4 *)((uint16_t *)a.out + base + dv) = v;
-                    } else {
-                        *(float4 *)((float *)a.out + base + dv) = make_float4(x0, x1, x2, x3);
-                    }
+            for (int g = 0; g < 4; ++g) {
+                const int dv = 32 * b + 8 * g + 4 * hb;
+                const float x0 = o[b][4 * g] * inv, x1 = o[b][4 * g + 1] * inv;
+                const float x2 = o[b][4 * g + 2] * inv, x3 = o[b][4 * g + 3] * inv;
+                if (a.out_bf16) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    bf16x4 v = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+                    *(bf16x4 *)((uint16_t *)a.out + base + dv) = v;
+                } else {
+                    *(float4 *)((float *)a.out + base + dv) = make_float4(x0, x1, x2, x3);
                 }
-            if (a.lse && hb == 0)
-                a.lse[(int64_t)h * a.n_q + row] = (m[qb] * c + __log2f(lt)) * 0.69314718055994531f;
-        }
+            }
+        if (a.lse && hb == 0)
+            a.lse[(int64_t)h * a.n_q + row] = (m * c + __log2f(lt)) * 0.69314718055994531f;
     }
 }
 
