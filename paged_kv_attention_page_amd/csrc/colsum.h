@@ -8,7 +8,8 @@
 // row_lanes) of the block's range, accumulating in registers (row order).
 // The row_lanes partials of a column are then added in lane order through
 // LDS, and one fp64 partial per (block, column) goes to the workspace.  A
-// second kernel adds the block partials in block order.  The inputs are bf16
+// second kernel adds the block partials in a fixed order
+// (reduce_partials_64).  The inputs are bf16
 // or fp32 values, so in practice every fp64 sum here is exact; the fixed
 // order makes repeated calls bitwise equal regardless.
 #pragma once
@@ -93,6 +94,37 @@ __device__ __forceinline__ void colsum_block(const uint4 *__restrict__ x, uint4 
         for (int lane = 0; lane < row_lanes; ++lane) s += lds[lane * hd + col];
         part[col] = s;
     }
+}
+
+// Sum the block partials partial[b][col] (b < blocks, row stride hd) for the
+// 64 columns c0 ... c0+63, with a block of 1024 threads: lane r = t/64 adds
+// blocks r, r+16, r+32, ... in that order, then the 16 lane sums are added in
+// lane order.  The order is fixed, so results are bitwise reproducible.
+// `lds` holds 16 * 64 doubles.  Returns the column sum in threads t < 64.
+__device__ __forceinline__ double reduce_partials_64(const double *__restrict__ partial, int blocks,
+                                                     int hd, int c0, double *lds) {
+    const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+    const int col = c0 + c;
+    double s = 0.0;
+    if (col < hd) {
+        const double *p = partial + col;
+        int b = r;
+        for (; b + 48 < blocks; b += 64) {
+            const double v0 = p[(int64_t)b * hd], v1 = p[(int64_t)(b + 16) * hd];
+            const double v2 = p[(int64_t)(b + 32) * hd], v3 = p[(int64_t)(b + 48) * hd];
+            s += v0;
+            s += v1;
+            s += v2;
+            s += v3;
+        }
+        for (; b < blocks; b += 16) s += p[(int64_t)b * hd];
+    }
+    lds[r * 64 + c] = s;
+    __syncthreads();
+    double tot = 0.0;
+    if (r == 0)
+        for (int k = 0; k < 16; ++k) tot += lds[k * 64 + c];
+    return tot;
 }
 
 }  // namespace wa

@@ -5,8 +5,8 @@
 //
 // Pass 1 (k_append_sum): one HBM pass over the page.  Every block copies its
 // row range of K (and V) into the pool slot and forms fp64 partial column
-// sums of K.  Pass 2 (k_colsum_finish): adds the block partials in block
-// order and divides by the row count.  Bound: HBM bandwidth; the algorithmic
+// sums of K.  Pass 2 (k_colsum_finish): adds the block partials in a fixed
+// order (16 lanes per column) and divides by the row count.  Bound: HBM bandwidth; the algorithmic
 // traffic is 2 x (K + V page bytes) plus 8 bytes per mean element written.
 #include "colsum.h"
 #include "wa_internal.h"
@@ -53,14 +53,15 @@ __global__ void k_append_sum(const uint4 *__restrict__ k_src, uint4 *__restrict_
                        blockIdx.x, lds, partial + (int64_t)blockIdx.x * chunks * VEC);
 }
 
-// out[col] = (sum over blocks b in order of partial[b][col]) / rows
-__global__ void k_colsum_finish(const double *__restrict__ partial, int blocks, int hd,
-                                int64_t rows, double *__restrict__ out) {
-    const int col = blockIdx.x * blockDim.x + threadIdx.x;
-    if (col >= hd) return;
-    double s = 0.0;
-    for (int b = 0; b < blocks; ++b) s += partial[(int64_t)b * hd + col];
-    out[col] = s / (double)rows;
+// out[col] = (sum of the block partials of col, fixed order) / rows; one
+// block of 1024 threads per 64 columns
+__global__ __launch_bounds__(1024) void k_colsum_finish(const double *__restrict__ partial,
+                                                        int blocks, int hd, int64_t rows,
+                                                        double *__restrict__ out) {
+    __shared__ double lds[16 * 64];
+    const int c0 = blockIdx.x * 64;
+    const double tot = reduce_partials_64(partial, blocks, hd, c0, lds);
+    if (threadIdx.x < 64 && c0 + (int)threadIdx.x < hd) out[c0 + threadIdx.x] = tot / (double)rows;
 }
 
 hipError_t launch_append(const wa_layout &L, const void *k_src, const void *v_src, void *k_pool,
@@ -89,7 +90,7 @@ hipError_t launch_append(const wa_layout &L, const void *k_src, const void *v_sr
                            p.chunks, p.row_lanes, p.rows_per_block, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_colsum_finish, dim3((unsigned)((hd + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_colsum_finish, dim3((unsigned)((hd + 63) / 64)), dim3(1024), 0, s,
                        (const double *)partial, p.blocks, (int)hd, (int64_t)L.page_tokens,
                        page_means + (int64_t)slot * hd);
     return hipGetLastError();

@@ -10,11 +10,13 @@
 //   stage 1  blocks [0, q_blocks): fp64 partial column sums of Q (HBM stream);
 //            blocks [q_blocks, q_blocks + n_chunks): cosine of the current
 //            prompt with one past chunk's prompt (prompt stage only);
-//   stage 2  one block per 64 columns: finish qbar for those columns, derive
-//            the candidate list (prompt stage: rank the chunks), and write
-//            each candidate's partial dot product over those columns;
-//   stage 3  one wavefront: add the column-group partials in order, scale,
-//            and take the top K_p by K_p rounds of a wavefront-shuffle argmax.
+//   stage 2  one block per 64 columns: finish qbar for those columns (16
+//            lanes per column, fixed order), derive the candidate list
+//            (prompt stage: rank the chunks), and write each candidate's
+//            partial dot product over those columns;
+//   stage 3  one block: add the column-group partials of each candidate with
+//            a butterfly (fixed order), scale, and take the top K_p by K_p
+//            rounds of a wavefront-shuffle argmax.
 #include <math.h>
 
 #include "colsum.h"
@@ -23,7 +25,8 @@
 namespace wa {
 
 static constexpr int kGroupCols = 64;     // columns per stage-2 block
-static constexpr int kStage2Threads = 256;
+static constexpr int kStage2Threads = 1024;
+static constexpr int kStage3Threads = 256;
 
 SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
                           int32_t n_chunks) {
@@ -144,7 +147,7 @@ __device__ void rank_chunks(const double *__restrict__ cosine, int n_chunks, int
     }
 }
 
-__global__ void k_select_stage2(const double *__restrict__ partial_q, int q_blocks, int hd,
+__global__ __launch_bounds__(kStage2Threads) void k_select_stage2(const double *__restrict__ partial_q, int q_blocks, int hd,
                                 int64_t n_q, const double *__restrict__ page_means,
                                 int max_pages, const int32_t *__restrict__ cand_in, int n_cand,
                                 const double *__restrict__ cosine, int n_chunks,
@@ -153,20 +156,19 @@ __global__ void k_select_stage2(const double *__restrict__ partial_q, int q_bloc
                                 int32_t *__restrict__ out_chunks, int32_t *__restrict__ out_cand,
                                 double *__restrict__ alpha_part) {
     __shared__ double qbar[kGroupCols];
+    __shared__ double red[16 * kGroupCols];
     __shared__ int kept[WA_MAX_CANDIDATES];
     const int t = threadIdx.x;
     const int g = blockIdx.x;
     const bool prompt = cosine != nullptr;
 
-    // qbar for this block's columns (block partials added in block order)
+    // qbar for this block's columns (block partials added in a fixed order)
+    const double tot = reduce_partials_64(partial_q, q_blocks, hd, g * kGroupCols, red);
     if (t < kGroupCols) {
         const int col = g * kGroupCols + t;
-        double s = 0.0;
-        if (col < hd)
-            for (int b = 0; b < q_blocks; ++b) s += partial_q[(int64_t)b * hd + col];
-        qbar[t] = col < hd ? s / (double)n_q : 0.0;
+        qbar[t] = col < hd ? tot / (double)n_q : 0.0;
     }
-    if (prompt && t < 64) rank_chunks(cosine, n_chunks, n_keep, kept);
+    if (prompt && t >= 64 && t < 128) rank_chunks(cosine, n_chunks, n_keep, kept);
     __syncthreads();
 
     // candidate id of position j
@@ -203,46 +205,49 @@ __global__ void k_select_stage2(const double *__restrict__ partial_q, int q_bloc
     }
 }
 
-// One wavefront.  Candidate j lives in lane j % 64, slot j / 64.
-__global__ void k_select_stage3(const double *__restrict__ alpha_part, int groups, int n_cand,
-                                const int32_t *__restrict__ cand_ws, int max_pages,
-                                double sqrt_d, int k_p,
-                                int32_t *__restrict__ out_idx, double *__restrict__ out_scores) {
+// One block.  alpha_j: lane g of a wavefront holds the column-group-g partial
+// of candidate j and a butterfly adds them (fixed order); wavefronts take
+// candidates in turn.  Then wavefront 0 takes the top K_p: candidate j lives
+// in lane j % 64, slot j / 64, and each round is a wavefront-shuffle argmax.
+__global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
+    const double *__restrict__ alpha_part, int groups, int n_cand,
+    const int32_t *__restrict__ cand_ws, int max_pages, double sqrt_d, int k_p,
+    int32_t *__restrict__ out_idx, double *__restrict__ out_scores) {
     __shared__ double sc[WA_MAX_CANDIDATES];
     __shared__ int ids[WA_MAX_CANDIDATES];
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    for (int j = wave; j < n_cand; j += kStage3Threads / 64) {
+        double v = lane < groups ? alpha_part[(int64_t)lane * n_cand + j] : 0.0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) {
+            const int id = cand_ws[j];
+            const bool valid = id >= 0 && id < max_pages;
+            const double s = valid ? v / sqrt_d : -INFINITY;
+            sc[j] = s;
+            ids[j] = id;
+            if (out_scores) out_scores[j] = s;
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
     const int per_lane = (n_cand + 63) / 64;   // <= 64
     unsigned long long taken = 0ull;
     for (int u = 0; u < per_lane; ++u) {
         const int j = lane + 64 * u;
-        if (j >= n_cand) {
-            taken |= 1ull << u;
-            continue;
-        }
-        const int id = cand_ws[j];
-        double s = 0.0;
-        for (int g = 0; g < groups; ++g) s += alpha_part[(int64_t)g * n_cand + j];
-        s = s / sqrt_d;
-        const bool valid = id >= 0 && id < max_pages;
-        if (!valid) {
-            s = -INFINITY;
-            taken |= 1ull << u;      // never selected
-        }
-        sc[u * 64 + lane] = s;
-        ids[u * 64 + lane] = id;
-        if (out_scores) out_scores[j] = s;
+        // past the end, or an id outside the pool: never selected
+        if (j >= n_cand || ids[j] < 0 || ids[j] >= max_pages) taken |= 1ull << u;
     }
     for (int r = 0; r < k_p; ++r) {
         double bs = 0.0;
         int bid = -1, bslot = -1;
         for (int u = 0; u < per_lane; ++u) {
             if ((taken >> u) & 1ull) continue;
-            const double s = sc[u * 64 + lane];
-            const int id = ids[u * 64 + lane];
-            if (ranks_before(s, id, bs, bid)) {
-                bs = s;
-                bid = id;
-                bslot = u * 64 + lane;
+            const int j = lane + 64 * u;
+            if (ranks_before(sc[j], ids[j], bs, bid)) {
+                bs = sc[j];
+                bid = ids[j];
+                bslot = j;
             }
         }
         wave_argmax(bs, bid, bslot);
@@ -293,7 +298,7 @@ hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const d
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    hipLaunchKernelGGL(k_select_stage3, dim3(1), dim3(64), 0, s, (const double *)alpha_part,
+    hipLaunchKernelGGL(k_select_stage3, dim3(1), dim3(kStage3Threads), 0, s, (const double *)alpha_part,
                        w.groups, n_cand, (const int32_t *)cand_ws, L.max_pages,
                        sqrt((double)L.head_dim), k_p, out_idx, out_scores);
     return hipGetLastError();
