@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attention_wan_kp4_traffic.json"),
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
+                                                      "k_attn_bf16_wan_kp4_hbm_traffic.txt"),
                     help="HBM traffic summary from rocprofv3 counters (optional)")
     return ap.parse_args()
 
@@ -58,8 +59,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the path is built and measured on one GPU's "
-              "share (see the sharding note in DESIGN.md); --gpus %d is not supported" % args.gpus,
-              file=sys.stderr)
+              "share of the work; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -135,36 +135,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # whole-step timing: K steps between two synchronisations
+    # K timed steps between two synchronisations; HIP events recorded on the
+    # launch stream around each call inside the same region give the
+    # per-kernel durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # per-kernel timing: HIP events on the launch stream around each call
-    per = {"append": [], "select": [], "gather": [], "attention": []}
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        step(evs)
-        torch.cuda.synchronize()
-        per["append"].append(evs[0].elapsed_time(evs[1]))
-        per["select"].append(evs[1].elapsed_time(evs[2]))
-        per["gather"].append(evs[2].elapsed_time(evs[3]))
-        per["attention"].append(evs[3].elapsed_time(evs[4]))
+    names = ("append", "select", "gather", "attention")
+    per = {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(names)}
     avg = {k: float(np.mean(v)) for k, v in per.items()}
     med = {k: float(np.median(v)) for k, v in per.items()}
 
     attn_tflops = flops / (avg["attention"] * 1e-3) / 1e12
     sg_gbps = (bytes_select + bytes_gather) / ((avg["select"] + avg["gather"]) * 1e-3) / 1e9
     value = flops / (ms_per_step * 1e-3) / 1e12
-
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            t = json.load(f)
-        traffic = t.get("bytes_per_launch")
+    traffic = load_traffic(args.traffic, wa.kernel_source("k_attn_bf16.hip"))
 
     result = {
         "metric": "block-attn TFLOP/s (MFMA %) + select/gather HBM GB/s at Kp=4, 49,920-tok KV",
@@ -217,6 +208,23 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h,
                                               args.cpu_seconds, torch)
     print(json.dumps(result), flush=True)
+
+
+def load_traffic(path, kernel_src):
+    """HBM bytes per attention launch from the rocprofv3 counter summary, or
+    None when there is none or it was taken on a different kernel source."""
+    if not path or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    import hashlib
+    if fields.get("kernel_source_sha256") != hashlib.sha256(kernel_src).hexdigest():
+        return None
+    return int(fields["bytes_per_launch"])
 
 
 def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, seconds, torch):

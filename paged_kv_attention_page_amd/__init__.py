@@ -67,6 +67,13 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def kernel_source(name: str) -> bytes:
+    """Bytes of one kernel source file (csrc/<name>), e.g. to tie a stored
+    profile to the kernel it was taken on."""
+    with open(os.path.join(_HERE, "csrc", name), "rb") as f:
+        return f.read()
+
+
 def load_library():
     """Load libwa.so (once).  Raises if it has not been built."""
     global _lib

@@ -38,30 +38,36 @@ __device__ __forceinline__ void accumulate_vec(double *acc, uint4 v) {
     }
 }
 
-// One block's share of the column sums, optionally copying the rows of up to
-// two arrays (K and V of a page) to their destinations on the way.
+// One block's share of the column sums: vectors [c0, c0 + group_chunks) of
+// the rows [r0, r1), optionally copying the rows of up to two arrays (K and V
+// of a page) to their destinations on the way.
 //   x      [rows][chunks] 16-byte vectors, summed (and copied to x_dst if set)
 //   y      [rows][chunks] vectors copied to y_dst (not summed), or null
-//   lds    row_lanes * chunks * VEC doubles of shared memory
-//   part   [chunks * VEC] doubles: this block's partial sums
+//   lds    row_lanes * group_chunks * VEC doubles of shared memory
+//   part   this row block's partial row ([hd] doubles); the block writes the
+//          columns of its group
+// Thread t owns vector c0 + t % group_chunks and rows r0 + t / group_chunks,
+// stepping by row_lanes, and accumulates in row order; the row_lanes partials
+// of a column are then added in lane order.
 template <bool BF16>
 __device__ __forceinline__ void colsum_block(const uint4 *__restrict__ x, uint4 *__restrict__ x_dst,
                                              const uint4 *__restrict__ y, uint4 *__restrict__ y_dst,
-                                             int64_t rows, int chunks, int row_lanes,
-                                             int rows_per_block, int block, double *lds,
-                                             double *__restrict__ part) {
+                                             int64_t rows, int chunks, int c0, int group_chunks,
+                                             int row_lanes, int rows_per_block, int row_block,
+                                             double *lds, double *__restrict__ part) {
     constexpr int VEC = BF16 ? 8 : 4;
     const int t = threadIdx.x;
-    const int hd = chunks * VEC;
-    const int64_t r0 = (int64_t)block * rows_per_block;
+    const int gw = min(group_chunks, chunks - c0) * VEC;   // columns in this group
+    const int64_t r0 = (int64_t)row_block * rows_per_block;
     const int64_t r1 = min(rows, r0 + rows_per_block);
     double acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
 
-    if (t < chunks * row_lanes) {
-        const int c = t % chunks;
-        const int lane = t / chunks;
+    const int cl = t % group_chunks;
+    const int lane = t / group_chunks;
+    if (lane < row_lanes && c0 + cl < chunks) {
+        const int c = c0 + cl;
         int64_t r = r0 + lane;
         // four rows in flight per thread
         for (; r + 3 * row_lanes < r1; r += 4 * row_lanes) {
@@ -86,13 +92,13 @@ __device__ __forceinline__ void colsum_block(const uint4 *__restrict__ x, uint4 
             accumulate_vec<BF16>(acc, xv);
         }
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) lds[lane * hd + c * VEC + e] = acc[e];
+        for (int e = 0; e < VEC; ++e) lds[lane * gw + cl * VEC + e] = acc[e];
     }
     __syncthreads();
-    for (int col = t; col < hd; col += blockDim.x) {
+    for (int col = t; col < gw; col += blockDim.x) {
         double s = 0.0;
-        for (int lane = 0; lane < row_lanes; ++lane) s += lds[lane * hd + col];
-        part[col] = s;
+        for (int ln = 0; ln < row_lanes; ++ln) s += lds[ln * gw + col];
+        part[c0 * VEC + col] = s;
     }
 }
 

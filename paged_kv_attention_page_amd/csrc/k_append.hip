@@ -13,28 +13,23 @@
 
 namespace wa {
 
-ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int max_blocks, int min_rows) {
+ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lane) {
     ColSumPlan p;
     p.vec = 16 / elem_bytes(dtype);
     p.chunks = (int)(hd / p.vec);
-    int lanes = 512 / p.chunks;
-    const int lds_cap = (int)(49152 / (hd * 8));
-    if (lanes > lds_cap) lanes = lds_cap;
-    if (lanes < 1) lanes = 1;
-    p.row_lanes = lanes;
-    p.threads = p.chunks * lanes;
-    if (p.threads < 64) p.threads = 64;
+    p.group_chunks = p.chunks < 64 ? p.chunks : 64;
+    p.groups = (p.chunks + p.group_chunks - 1) / p.group_chunks;
+    p.row_lanes = 256 / p.group_chunks;
+    p.threads = p.group_chunks * p.row_lanes;
     p.threads = (p.threads + 63) / 64 * 64;
-    int64_t blocks = (rows + min_rows - 1) / min_rows;
-    if (blocks > max_blocks) blocks = max_blocks;
-    if (blocks < 1) blocks = 1;
-    p.rows_per_block = (int)((rows + blocks - 1) / blocks);
+    p.rows_per_block = p.row_lanes * rows_per_lane;
     p.blocks = (int)((rows + p.rows_per_block - 1) / p.rows_per_block);
+    if (p.blocks < 1) p.blocks = 1;
     return p;
 }
 
 static ColSumPlan append_plan(int32_t dtype, int64_t hd, int64_t page_tokens) {
-    return colsum_plan(dtype, hd, page_tokens, 1024, 32);
+    return colsum_plan(dtype, hd, page_tokens, 16);
 }
 
 size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens) {
@@ -43,14 +38,15 @@ size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens) {
 }
 
 template <bool BF16>
-__global__ void k_append_sum(const uint4 *__restrict__ k_src, uint4 *__restrict__ k_dst,
-                             const uint4 *__restrict__ v_src, uint4 *__restrict__ v_dst,
-                             int64_t rows, int chunks, int row_lanes, int rows_per_block,
-                             double *__restrict__ partial) {
-    extern __shared__ double lds[];
+__global__ __launch_bounds__(256) void k_append_sum(
+    const uint4 *__restrict__ k_src, uint4 *__restrict__ k_dst, const uint4 *__restrict__ v_src,
+    uint4 *__restrict__ v_dst, int64_t rows, int chunks, int group_chunks, int row_lanes,
+    int rows_per_block, double *__restrict__ partial) {
+    __shared__ double lds[256 * (BF16 ? 8 : 4)];
     constexpr int VEC = BF16 ? 8 : 4;
-    colsum_block<BF16>(k_src, k_dst, v_src, v_dst, rows, chunks, row_lanes, rows_per_block,
-                       blockIdx.x, lds, partial + (int64_t)blockIdx.x * chunks * VEC);
+    colsum_block<BF16>(k_src, k_dst, v_src, v_dst, rows, chunks, blockIdx.x * group_chunks,
+                       group_chunks, row_lanes, rows_per_block, blockIdx.y, lds,
+                       partial + (int64_t)blockIdx.y * chunks * VEC);
 }
 
 // out[col] = (sum of the block partials of col, fixed order) / rows; one
@@ -78,16 +74,16 @@ hipError_t launch_append(const wa_layout &L, const void *k_src, const void *v_sr
     uint4 *v_dst = v_read ? (uint4 *)v_slot : nullptr;
 
     const ColSumPlan p = append_plan(L.dtype, hd, L.page_tokens);
-    const size_t lds = (size_t)p.row_lanes * hd * sizeof(double);
     double *partial = (double *)ws;
+    const dim3 grid((unsigned)p.groups, (unsigned)p.blocks);
     if (L.dtype == WA_BF16)
-        hipLaunchKernelGGL(k_append_sum<true>, dim3(p.blocks), dim3(p.threads), lds, s,
-                           (const uint4 *)k_src, k_dst, v_read, v_dst, (int64_t)L.page_tokens,
-                           p.chunks, p.row_lanes, p.rows_per_block, partial);
+        hipLaunchKernelGGL(k_append_sum<true>, grid, dim3(p.threads), 0, s, (const uint4 *)k_src,
+                           k_dst, v_read, v_dst, (int64_t)L.page_tokens, p.chunks, p.group_chunks,
+                           p.row_lanes, p.rows_per_block, partial);
     else
-        hipLaunchKernelGGL(k_append_sum<false>, dim3(p.blocks), dim3(p.threads), lds, s,
-                           (const uint4 *)k_src, k_dst, v_read, v_dst, (int64_t)L.page_tokens,
-                           p.chunks, p.row_lanes, p.rows_per_block, partial);
+        hipLaunchKernelGGL(k_append_sum<false>, grid, dim3(p.threads), 0, s, (const uint4 *)k_src,
+                           k_dst, v_read, v_dst, (int64_t)L.page_tokens, p.chunks, p.group_chunks,
+                           p.row_lanes, p.rows_per_block, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_colsum_finish, dim3((unsigned)((hd + 63) / 64)), dim3(1024), 0, s,

@@ -4,19 +4,25 @@
 //   alpha_j = sum_{h,c} qbar[h,c] * kbar_j[h,c] / sqrt(d),
 //   idx = top-K_p candidates by (alpha desc, page id asc).
 // Everything after the bf16/fp32 inputs is fp64, with fixed reduction orders,
-// so the selection is decided in the same precision as the fp64 reference.
+// so the selection is decided in the same precision as the fp64 reference,
+// and repeated calls are bitwise equal.
 //
 // Three launches, no host synchronisation:
-//   stage 1  blocks [0, q_blocks): fp64 partial column sums of Q (HBM stream);
-//            blocks [q_blocks, q_blocks + n_chunks): cosine of the current
-//            prompt with one past chunk's prompt (prompt stage only);
+//   stage 1  blocks (column group, row block): fp64 partial column sums of Q
+//            (HBM stream); then one block per past chunk: cosine of the
+//            current prompt with that chunk's prompt (prompt stage only).
 //   stage 2  one block per 64 columns: finish qbar for those columns (16
 //            lanes per column, fixed order), derive the candidate list
 //            (prompt stage: rank the chunks), and write each candidate's
-//            partial dot product over those columns;
-//   stage 3  one block: add the column-group partials of each candidate with
-//            a butterfly (fixed order), scale, and take the top K_p by K_p
+//            partial dot product over those columns.
+//   stage 3  one block: alpha_j = the column-group partials of candidate j
+//            added in group order, scaled; then the top K_p.  Up to
+//            blockDim.x candidates, each thread counts the candidates that
+//            rank before its own (one pass, no shuffles); beyond that, K_p
 //            rounds of a wavefront-shuffle argmax.
+// A kernel boundary, not a device-scope fence and counter, hands data from
+// one stage to the next: with one L2 per XCD, the fence's L2 write-back and
+// invalidate plus the counter's round trip cost more than a boundary.
 #include <math.h>
 
 #include "colsum.h"
@@ -26,12 +32,13 @@ namespace wa {
 
 static constexpr int kGroupCols = 64;     // columns per stage-2 block
 static constexpr int kStage2Threads = 1024;
-static constexpr int kStage3Threads = 256;
+static constexpr int kStage3Threads = 1024;
+static constexpr int kQRowsPerLane = 8;   // rows each stage-1 lane adds
 
 SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
                           int32_t n_chunks) {
     SelectWs w;
-    w.q_plan = colsum_plan(dtype, hd, n_q, 256, 16);
+    w.q_plan = colsum_plan(dtype, hd, n_q, kQRowsPerLane);
     w.groups = (int)((hd + kGroupCols - 1) / kGroupCols);
     size_t off = 0;
     w.partial_q = off;
@@ -46,25 +53,27 @@ SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand
     return w;
 }
 
-// (score desc, id asc) total order; an id < 0 marks "no item" and ranks last.
-__device__ __forceinline__ bool ranks_before(double sa, int ia, double sb, int ib) {
+// Total order of (score, id, position) items: score descending, then id
+// ascending, then list position ascending (a repeated id is taken once per
+// occurrence, in list order).  An id < 0 marks "no item" and ranks last.
+__device__ __forceinline__ bool ranks_before(double sa, int ia, int ja, double sb, int ib, int jb) {
     if (ib < 0) return ia >= 0;
     if (ia < 0) return false;
-    return sa > sb || (sa == sb && ia < ib);
+    return sa > sb || (sa == sb && (ia < ib || (ia == ib && ja < jb)));
 }
 
 // Butterfly argmax over the 64 lanes of a wavefront; every lane ends with the
 // same winner because the order is total.
-__device__ __forceinline__ void wave_argmax(double &s, int &id, int &src) {
+__device__ __forceinline__ void wave_argmax(double &s, int &id, int &pos) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const double os = __shfl_xor(s, off, 64);
         const int oid = __shfl_xor(id, off, 64);
-        const int osrc = __shfl_xor(src, off, 64);
-        if (ranks_before(os, oid, s, id)) {
+        const int opos = __shfl_xor(pos, off, 64);
+        if (ranks_before(os, oid, opos, s, id, pos)) {
             s = os;
             id = oid;
-            src = osrc;
+            pos = opos;
         }
     }
 }
@@ -91,29 +100,33 @@ __device__ void block_sum3(double &a, double &b, double &c, double *sh) {
     c = sh[2 * blockDim.x];
 }
 
+// Blocks [0, groups * q_blocks): column sums of Q, block b -> (column group
+// b % groups, row block b / groups).  Blocks after those: prompt cosines.
 template <bool BF16>
-__global__ void k_select_stage1(const uint4 *__restrict__ q, int64_t n_q, int chunks,
-                                int row_lanes, int rows_per_block, int q_blocks,
-                                double *__restrict__ partial_q,
-                                const float *__restrict__ chunk_prompts,
-                                const float *__restrict__ cur_prompt, int emb_dim,
-                                double *__restrict__ cosine) {
-    extern __shared__ double lds[];
+__global__ __launch_bounds__(256) void k_select_stage1(
+    const uint4 *__restrict__ q, int64_t n_q, int chunks, int group_chunks, int groups,
+    int row_lanes, int rows_per_block, int q_blocks, double *__restrict__ partial_q,
+    const float *__restrict__ chunk_prompts, const float *__restrict__ cur_prompt, int emb_dim,
+    double *__restrict__ cosine) {
+    __shared__ double lds[256 * (BF16 ? 8 : 4)];   // >= 3 * blockDim.x for block_sum3
     constexpr int VEC = BF16 ? 8 : 4;
-    if ((int)blockIdx.x < q_blocks) {
-        colsum_block<BF16>(q, nullptr, nullptr, nullptr, n_q, chunks, row_lanes, rows_per_block,
-                           blockIdx.x, lds, partial_q + (int64_t)blockIdx.x * chunks * VEC);
+    const int b = blockIdx.x;
+    if (b < groups * q_blocks) {
+        const int g = b % groups, rb = b / groups;
+        colsum_block<BF16>(q, nullptr, nullptr, nullptr, n_q, chunks, g * group_chunks,
+                           group_chunks, row_lanes, rows_per_block, rb, lds,
+                           partial_q + (int64_t)rb * chunks * VEC);
         return;
     }
     // prompt stage: cosine of the current prompt with chunk m's prompt
-    const int m = blockIdx.x - q_blocks;
+    const int m = b - groups * q_blocks;
     const float *pm = chunk_prompts + (int64_t)m * emb_dim;
     double dot = 0.0, nn = 0.0, pp = 0.0;
     for (int e = threadIdx.x; e < emb_dim; e += blockDim.x) {
         const double a = (double)cur_prompt[e];
-        const double b = (double)pm[e];
-        dot += a * b;
-        nn += b * b;
+        const double c = (double)pm[e];
+        dot += a * c;
+        nn += c * c;
         pp += a * a;
     }
     block_sum3(dot, nn, pp, lds);
@@ -129,18 +142,18 @@ __device__ void rank_chunks(const double *__restrict__ cosine, int n_chunks, int
     unsigned long long mine = 0ull;
     for (int r = 0; r < n_keep; ++r) {
         double bs = 0.0;
-        int bid = -1, bsrc = -1;
+        int bid = -1, bpos = -1;
         for (int u = 0; u < per_lane; ++u) {
             const int m = lane + 64 * u;
             if (m >= n_chunks || ((mine >> u) & 1ull)) continue;
             const double cs = cosine[m];
-            if (ranks_before(cs, m, bs, bid)) {
+            if (ranks_before(cs, m, m, bs, bid, bpos)) {
                 bs = cs;
                 bid = m;
-                bsrc = u;
+                bpos = m;
             }
         }
-        wave_argmax(bs, bid, bsrc);
+        wave_argmax(bs, bid, bpos);
         // the lane that owns the winner marks it taken
         if (bid >= 0 && (bid & 63) == lane) mine |= 1ull << (bid / 64);
         if (lane == 0) kept[r] = bid;
@@ -203,55 +216,78 @@ __global__ __launch_bounds__(kStage2Threads) void k_select_stage2(const double *
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
         if (lane == 0) alpha_part[(int64_t)g * n_cand + j] = v;
     }
+
 }
 
-// One block.  alpha_j: lane g of a wavefront holds the column-group-g partial
-// of candidate j and a butterfly adds them (fixed order); wavefronts take
-// candidates in turn.  Then wavefront 0 takes the top K_p: candidate j lives
-// in lane j % 64, slot j / 64, and each round is a wavefront-shuffle argmax.
+// One block of kStage3Threads threads.
 __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
     const double *__restrict__ alpha_part, int groups, int n_cand,
     const int32_t *__restrict__ cand_ws, int max_pages, double sqrt_d, int k_p,
     int32_t *__restrict__ out_idx, double *__restrict__ out_scores) {
     __shared__ double sc[WA_MAX_CANDIDATES];
     __shared__ int ids[WA_MAX_CANDIDATES];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    for (int j = wave; j < n_cand; j += kStage3Threads / 64) {
-        double v = lane < groups ? alpha_part[(int64_t)lane * n_cand + j] : 0.0;
+    const int t = threadIdx.x;
+    // alpha_j: group partials added in group order; an id outside the pool
+    // scores -inf and is never selected
+    for (int j = t; j < n_cand; j += blockDim.x) {
+        double v = 0.0;
+        for (int g0 = 0; g0 < groups; g0 += 16) {
+            double x[16];   // 16 loads in flight, then added in group order
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        if (lane == 0) {
-            const int id = cand_ws[j];
-            const bool valid = id >= 0 && id < max_pages;
-            const double s = valid ? v / sqrt_d : -INFINITY;
-            sc[j] = s;
-            ids[j] = id;
-            if (out_scores) out_scores[j] = s;
+            for (int u = 0; u < 16; ++u)
+                x[u] = g0 + u < groups ? alpha_part[(int64_t)(g0 + u) * n_cand + j] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (g0 + u < groups) v += x[u];
         }
+        const int id = cand_ws[j];
+        const bool valid = id >= 0 && id < max_pages;
+        const double s = valid ? v / sqrt_d : -INFINITY;
+        sc[j] = s;
+        ids[j] = valid ? id : -1;
+        if (out_scores) out_scores[j] = s;
     }
     __syncthreads();
-    if (wave != 0) return;
+
+    if (n_cand <= (int)blockDim.x) {
+        // rank of candidate t = number of candidates ordered before it
+        const bool mine = t < n_cand && ids[t] >= 0;
+        const int n_valid = __syncthreads_count(mine);
+        if (mine) {
+            const double s = sc[t];
+            const int id = ids[t];
+            int rank = 0;
+            for (int i = 0; i < n_cand; ++i) rank += ranks_before(sc[i], ids[i], i, s, id, t);
+            if (rank < k_p) out_idx[rank] = id;
+        }
+        for (int r = n_valid + t; r < k_p; r += blockDim.x) out_idx[r] = -1;
+        return;
+    }
+
+    // many candidates: wavefront 0 takes K_p rounds of an argmax; candidate
+    // j lives in lane j % 64, slot j / 64
+    if (t >= 64) return;
+    const int lane = t;
     const int per_lane = (n_cand + 63) / 64;   // <= 64
     unsigned long long taken = 0ull;
     for (int u = 0; u < per_lane; ++u) {
         const int j = lane + 64 * u;
-        // past the end, or an id outside the pool: never selected
-        if (j >= n_cand || ids[j] < 0 || ids[j] >= max_pages) taken |= 1ull << u;
+        if (j >= n_cand || ids[j] < 0) taken |= 1ull << u;
     }
     for (int r = 0; r < k_p; ++r) {
         double bs = 0.0;
-        int bid = -1, bslot = -1;
+        int bid = -1, bpos = -1;
         for (int u = 0; u < per_lane; ++u) {
             if ((taken >> u) & 1ull) continue;
             const int j = lane + 64 * u;
-            if (ranks_before(sc[j], ids[j], bs, bid)) {
+            if (ranks_before(sc[j], ids[j], j, bs, bid, bpos)) {
                 bs = sc[j];
                 bid = ids[j];
-                bslot = j;
+                bpos = j;
             }
         }
-        wave_argmax(bs, bid, bslot);
-        if (bslot >= 0 && (bslot & 63) == lane) taken |= 1ull << (bslot >> 6);
+        wave_argmax(bs, bid, bpos);
+        if (bpos >= 0 && (bpos & 63) == lane) taken |= 1ull << (bpos >> 6);
         if (lane == 0) out_idx[r] = bid;     // -1 when nothing valid is left
     }
 }
@@ -270,21 +306,20 @@ hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const d
     int32_t *cand_ws = (int32_t *)(base + w.cand);
     const ColSumPlan &p = w.q_plan;
 
-    size_t lds = (size_t)p.row_lanes * hd * sizeof(double);
-    if (prompt && lds < 3 * (size_t)p.threads * sizeof(double))
-        lds = 3 * (size_t)p.threads * sizeof(double);
-    const int blocks1 = p.blocks + n_chunks;
+    const int blocks1 = p.groups * p.blocks + n_chunks;
     const float *cp = prompt ? prompt->chunk_prompts : nullptr;
     const float *cur = prompt ? prompt->cur_prompt : nullptr;
     const int emb = prompt ? prompt->emb_dim : 0;
     if (L.dtype == WA_BF16)
-        hipLaunchKernelGGL(k_select_stage1<true>, dim3(blocks1), dim3(p.threads), lds, s,
-                           (const uint4 *)q, (int64_t)n_q, p.chunks, p.row_lanes,
-                           p.rows_per_block, p.blocks, partial_q, cp, cur, emb, cosine);
+        hipLaunchKernelGGL(k_select_stage1<true>, dim3(blocks1), dim3(p.threads), 0, s,
+                           (const uint4 *)q, (int64_t)n_q, p.chunks, p.group_chunks, p.groups,
+                           p.row_lanes, p.rows_per_block, p.blocks, partial_q, cp, cur, emb,
+                           cosine);
     else
-        hipLaunchKernelGGL(k_select_stage1<false>, dim3(blocks1), dim3(p.threads), lds, s,
-                           (const uint4 *)q, (int64_t)n_q, p.chunks, p.row_lanes,
-                           p.rows_per_block, p.blocks, partial_q, cp, cur, emb, cosine);
+        hipLaunchKernelGGL(k_select_stage1<false>, dim3(blocks1), dim3(p.threads), 0, s,
+                           (const uint4 *)q, (int64_t)n_q, p.chunks, p.group_chunks, p.groups,
+                           p.row_lanes, p.rows_per_block, p.blocks, partial_q, cp, cur, emb,
+                           cosine);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -298,9 +333,9 @@ hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const d
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    hipLaunchKernelGGL(k_select_stage3, dim3(1), dim3(kStage3Threads), 0, s, (const double *)alpha_part,
-                       w.groups, n_cand, (const int32_t *)cand_ws, L.max_pages,
-                       sqrt((double)L.head_dim), k_p, out_idx, out_scores);
+    hipLaunchKernelGGL(k_select_stage3, dim3(1), dim3(kStage3Threads), 0, s,
+                       (const double *)alpha_part, w.groups, n_cand, (const int32_t *)cand_ws,
+                       L.max_pages, sqrt((double)L.head_dim), k_p, out_idx, out_scores);
     return hipGetLastError();
 }
 

@@ -18,19 +18,23 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 // column sums (page mean key, chunk mean query)
 //
-// A column-sum launch splits the rows of a [rows][hd] array into `blocks`
-// row ranges; each block writes one fp64 partial sum per column, and a second
-// kernel adds the partials in block order.  `vec` = elements per 16-byte
-// vector, `chunks` = hd / vec vectors per row, `row_lanes` = rows read at once.
+// A column-sum launch is a 2-D grid: blockIdx.x picks a group of up to 64
+// 16-byte column vectors, blockIdx.y a range of rows.  Each block writes one
+// fp64 partial sum per column of its group for its row range (partial layout
+// [row_blocks][hd]); a second kernel adds the partials of a column in a fixed
+// order.  `vec` = elements per 16-byte vector, `chunks` = hd / vec vectors per
+// row, `group_chunks` = vectors per block, `row_lanes` = rows read at once.
 struct ColSumPlan {
     int vec;
     int chunks;
+    int group_chunks;
+    int groups;
     int row_lanes;
     int threads;
     int rows_per_block;
-    int blocks;
+    int blocks;   // row blocks
 };
-ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int max_blocks, int min_rows);
+ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lane);
 
 // ---------------------------------------------------------------------------
 // workspace layouts

@@ -151,6 +151,38 @@ def test_select_skips_out_of_range_candidates():
     assert np.isneginf(s[1]) and np.isneginf(s[2])
 
 
+@pytest.mark.parametrize("n_cand,k_p", [(1024, 7), (1025, 7), (3000, 40), (11, 3)])
+def test_select_long_candidate_lists_with_repeats(n_cand, k_p):
+    """Both top-K paths (one thread per candidate up to 1,024 candidates, an
+    argmax per rank beyond): a repeated page id is selected once per
+    occurrence, and ids outside the pool are never selected."""
+    wl = BF
+    run = _pool_with_pages(wl, wl.n_pages)
+    q = W.chunk_qkv(wl, 0, 0)[0]
+    rng = np.random.default_rng([n_cand, k_p])
+    cand = rng.integers(0, wl.n_pages, n_cand).astype(np.int32)
+    cand[rng.choice(n_cand, n_cand // 7, replace=False)] = 99     # outside the pool
+    say("select long cand", n_cand, k_p)
+    idx = wa.wa_select_pages(run.L, to_device(q), run.means, k_p,
+                             cand=torch.from_numpy(cand).cuda())
+    valid = cand[cand < wl.n_pages]
+    ref = oracle.select_pages(q, run.oracle_means(range(wl.n_pages)), min(k_p, valid.size),
+                              cand=valid)["idx"].tolist()
+    assert idx.cpu().numpy().tolist() == ref + [-1] * (k_p - len(ref))
+
+
+@pytest.mark.parametrize("n_cand", [11, 1031])
+def test_select_fewer_valid_candidates_than_k_p(n_cand):
+    wl = BF
+    run = _pool_with_pages(wl, wl.n_pages)
+    q = W.chunk_qkv(wl, 0, 0)[0]
+    cand = np.full(n_cand, 99, np.int32)
+    cand[n_cand // 2] = 2
+    say("select sparse cand", n_cand)
+    idx = wa.wa_select_pages(run.L, to_device(q), run.means, 3, cand=torch.from_numpy(cand).cuda())
+    assert idx.cpu().numpy().tolist() == [2, -1, -1]
+
+
 def test_gather_skips_out_of_range_index():
     wl = BF
     run = _pool_with_pages(wl, wl.n_pages)
