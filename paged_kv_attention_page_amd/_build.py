@@ -21,10 +21,13 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 
 
 # Per-source flags.  The attention kernel asks for the VGPR form of the
-# matrix-core instructions: its score tiles feed vector ALU work directly, and
-# the long-lived query fragments and output accumulators are pinned to AGPRs
-# in the source.
-EXTRA_FLAGS = {"k_attn_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+# matrix-core instructions (its score tiles feed vector ALU work directly) and
+# uses no AGPRs at all, so the whole 256-register budget of two wavefronts per
+# SIMD goes to VGPRs.  It runs without the IEEE mode bit and assumes no NaNs
+# (inputs are finite), so maxima of matrix-core results need no
+# canonicalising instruction before each v_max.
+EXTRA_FLAGS = {"k_attn_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee",
+                                   "-fno-honor-nans"]}
 
 
 def hipcc() -> str:

@@ -28,8 +28,10 @@
 //    matches P.
 //  * Software pipeline per wave: the Q K^T products of the next sub-tile are
 //    interleaved with the exponentials of the current one, and the P V
-//    products with the next sub-tile's max (sched_group_barrier patterns), so
-//    matrix-core and vector work overlap; the output is only rescaled when a
+//    products with the next sub-tile's max, so matrix-core and vector work
+//    overlap (the instruction order inside a region is left to the compiler:
+//    with two wavefronts per SIMD, the other wavefront fills the gaps); all
+//    operands and accumulators live in VGPRs.  The output is only rescaled when a
 //    query's max grows by more than 2^8 in the exp2 domain (exact either way:
 //    the final division uses the same reference max).
 #include <math.h>
@@ -76,43 +78,41 @@ struct AttnArgs {
 };
 
 // One 16-byte-per-lane DMA from global memory into LDS: lane i's 16 bytes
-// land at lds_base + 16 i.  Issued through inline assembly so that the
-// compiler does not insert its own (conservative) waits for the copy before
-// unrelated LDS reads; the kernel waits for the copies itself (vmcnt) before
-// the barrier that publishes a tile.  Nothing else in the kernel uses m0.
+// land at lds_base + OFF + 16 i, where lds_base is a wave-uniform SGPR and OFF
+// a compile-time offset (m0 is set with one scalar add).  Issued through
+// inline assembly so that the compiler does not insert its own (conservative)
+// waits for the copy before unrelated LDS reads; the kernel waits for the
+// copies itself (vmcnt) before the barrier that publishes a tile.  Nothing
+// else in the kernel uses m0.
+template <unsigned OFF>
 __device__ __forceinline__ void dma16(const void *gptr, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_add_u32 m0, %0, %2\n\tglobal_load_lds_dwordx4 %1, off"
                  :
-                 : "s"(lds_base), "v"(gptr)
+                 : "s"(lds_base), "v"(gptr), "i"(OFF)
                  : "memory", "m0");
 }
 // The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset: the per-lane offsets of a tile never change, so issuing a tile
 // costs no vector instructions beyond the copies themselves.
+template <unsigned OFF>
 __device__ __forceinline__ void dma16_sbase(const void *sbase, unsigned voff, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "s"(lds_base), "v"(voff), "s"(sbase), "i"(OFF)
                  : "memory", "m0");
+}
+// A wave-uniform pointer kept in SGPRs: the empty asm makes the value opaque,
+// so the compiler cannot re-load it from the kernel arguments (with a wait on
+// every outstanding LDS read) each time it is used.
+template <typename T>
+__device__ __forceinline__ T *sgpr_ptr(T *p) {
+    uint64_t x = (uint64_t)(uintptr_t)p;
+    asm volatile("" : "+s"(x));
+    return (T *)(uintptr_t)x;
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
-
-// Pin a value at this point of the instruction stream: it must be computed
-// before here and may not sink below.  Used with sched_barrier(0) to lay out
-// the matrix-core / vector interleave of the fused regions explicitly.
-template <typename T>
-__device__ __forceinline__ void pin(T &v) {
-    asm volatile("" : "+v"(v));
-}
-// Ask for a value to live in accumulation registers (AGPRs): the matrix cores
-// read their operands and accumulators from there, and it leaves the vector
-// registers to the softmax.
-template <typename T>
-__device__ __forceinline__ void pin_acc(T &v) {
-    asm volatile("" : "+a"(v));
-}
 
 __device__ __forceinline__ unsigned lds_addr(const void *p) {
     return (unsigned)(uintptr_t)(const WA_LDS void *)p;
@@ -127,17 +127,11 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One LDS variable per ring stage: every access below names its stage at
-// compile time, so the compiler can tell the stage being refilled by DMA from
-// the stages being read, and does not wait for the refill before reading.
-__shared__ __attribute__((aligned(1024))) uint16_t lds_k0[kTileElems];
-__shared__ __attribute__((aligned(1024))) uint16_t lds_k1[kTileElems];
-__shared__ __attribute__((aligned(1024))) uint16_t lds_k2[kTileElems];
-__shared__ __attribute__((aligned(1024))) uint16_t lds_k3[kTileElems];
-__shared__ __attribute__((aligned(1024))) uint16_t lds_v0[kTileElems];
-__shared__ __attribute__((aligned(1024))) uint16_t lds_v1[kTileElems];
-__shared__ __attribute__((aligned(1024))) uint16_t lds_v2[kTileElems];
-__shared__ __attribute__((aligned(1024))) uint16_t lds_v3[kTileElems];
+// The K/V ring in one LDS array: the kStages K tiles, then the kStages V
+// tiles.  Every access names its stage at compile time, so each address is a
+// per-lane (or wave-uniform) base plus a constant.
+static constexpr unsigned kTileBytes = kTileElems * 2;
+__shared__ __attribute__((aligned(1024))) uint16_t lds_ring[2 * kStages * kTileElems];
 
 template <int S>
 struct StageTag {
@@ -147,17 +141,12 @@ struct StageTag {
 template <int S>
 __device__ __forceinline__ uint16_t *kst() {
     static_assert(S >= 0 && S < kStages, "stage");
-    if constexpr (S == 0) return lds_k0;
-    else if constexpr (S == 1) return lds_k1;
-    else if constexpr (S == 2) return lds_k2;
-    else return lds_k3;
+    return lds_ring + S * kTileElems;
 }
 template <int S>
 __device__ __forceinline__ uint16_t *vst() {
-    if constexpr (S == 0) return lds_v0;
-    else if constexpr (S == 1) return lds_v1;
-    else if constexpr (S == 2) return lds_v2;
-    else return lds_v3;
+    static_assert(S >= 0 && S < kStages, "stage");
+    return lds_ring + (kStages + S) * kTileElems;
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -179,7 +168,10 @@ void k_attn_bf16(AttnArgs a) {
     // tiles, 4 rows (1 KB) per instruction; lane -> (row 8w+4i+lane/16, slot lane%16)
     const int ld_row0 = kRowsPerWave * wave + (lane >> 4);
     const int ld_slot = lane & 15;
-    const unsigned ld_base = __builtin_amdgcn_readfirstlane(kRowsPerWave * wave * kD * 2);
+    const unsigned ld_base =
+        __builtin_amdgcn_readfirstlane(lds_addr(lds_ring) + kRowsPerWave * wave * kD * 2);
+    const uint16_t *const k_ctx = sgpr_ptr(a.k_ctx), *const v_ctx = sgpr_ptr(a.v_ctx);
+    const uint16_t *const k_own = sgpr_ptr(a.k_own), *const v_own = sgpr_ptr(a.v_own);
     // per-lane byte offsets of this lane's 16 bytes within a tile whose first
     // row is at a uniform base (fast path: the tile lies inside one segment)
     unsigned koff[kCopies], voff[kCopies];
@@ -190,27 +182,30 @@ void k_attn_bf16(AttnArgs a) {
         koff[i] = rowb + 16u * (unsigned)(ld_slot ^ (row & 15));
         voff[i] = rowb + 16u * (unsigned)(ld_slot ^ (4 * (row & 3)));
     }
-    auto issue_tile = [&](int t, uint16_t *ks, uint16_t *vs) __attribute__((always_inline)) {
+    static_assert(kCopies == 2, "issue_tile writes two 1 KB copies per tensor");
+    auto issue_tile = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+        constexpr unsigned S = decltype(stage_tag)::value;
+        constexpr unsigned OK = S * kTileBytes, OV = (kStages + S) * kTileBytes;
+        constexpr unsigned ROWS4 = 4 * kD * 2;    // four tile rows
         const int key0 = t * kBN;
-        const unsigned lk = lds_addr(ks) + ld_base, lv = lds_addr(vs) + ld_base;
         const uint16_t *kb = nullptr, *vb = nullptr;
         if (key0 + kBN <= a.n_ctx) {
-            kb = a.k_ctx + (int64_t)key0 * hd;
-            vb = a.v_ctx + (int64_t)key0 * hd;
+            kb = k_ctx + (int64_t)key0 * hd;
+            vb = v_ctx + (int64_t)key0 * hd;
         } else if (key0 >= a.n_ctx && key0 + kBN <= n_keys) {
-            kb = a.k_own + (int64_t)(key0 - a.n_ctx) * hd;
-            vb = a.v_own + (int64_t)(key0 - a.n_ctx) * hd;
+            kb = k_own + (int64_t)(key0 - a.n_ctx) * hd;
+            vb = v_own + (int64_t)(key0 - a.n_ctx) * hd;
         }
         if (kb) {
-#pragma unroll
-            for (int i = 0; i < kCopies; ++i) {
-                dma16_sbase(kb, koff[i], lk + 4 * i * kD * 2);
-                dma16_sbase(vb, voff[i], lv + 4 * i * kD * 2);
-            }
+            dma16_sbase<OK>(kb, koff[0], ld_base);
+            dma16_sbase<OV>(vb, voff[0], ld_base);
+            dma16_sbase<OK + ROWS4>(kb, koff[1], ld_base);
+            dma16_sbase<OV + ROWS4>(vb, voff[1], ld_base);
             return;
         }
         // tile across the ctx/own boundary or past the end: per-lane rows
         asm volatile("; dma slow path" ::: "memory");
+        const uint16_t *kr[kCopies], *vr[kCopies];
 #pragma unroll
         for (int i = 0; i < kCopies; ++i) {
             const int row = ld_row0 + 4 * i;
@@ -218,11 +213,13 @@ void k_attn_bf16(AttnArgs a) {
             n = n < n_keys ? n : n_keys - 1;           // rows past the end repeat the last key
             const bool in_ctx = n < a.n_ctx;
             const int64_t off = (int64_t)(in_ctx ? n : n - a.n_ctx) * hd + h * kD;
-            const uint16_t *kr = (in_ctx ? a.k_ctx : a.k_own) + off;
-            const uint16_t *vr = (in_ctx ? a.v_ctx : a.v_own) + off;
-            dma16(kr + 8 * (ld_slot ^ (row & 15)), lk + 4 * i * kD * 2);
-            dma16(vr + 8 * (ld_slot ^ (4 * (row & 3))), lv + 4 * i * kD * 2);
+            kr[i] = (in_ctx ? k_ctx : k_own) + off + 8 * (ld_slot ^ (row & 15));
+            vr[i] = (in_ctx ? v_ctx : v_own) + off + 8 * (ld_slot ^ (4 * (row & 3)));
         }
+        dma16<OK>(kr[0], ld_base);
+        dma16<OV>(vr[0], ld_base);
+        dma16<OK + ROWS4>(kr[1], ld_base);
+        dma16<OV + ROWS4>(vr[1], ld_base);
     };
 
     // ---- this wavefront's 32 queries as B operands: qf[st] = Q[q0+lr][16st+8hb ..+7]
@@ -235,7 +232,6 @@ void k_attn_bf16(AttnArgs a) {
                 qf[st] = *(const bf16x8 *)(a.q + (int64_t)row * hd + h * kD + 16 * st + 8 * hb);
             else
                 qf[st] = (bf16x8)(__bf16)0.f;
-            pin_acc(qf[st]);
         }
     }
 
@@ -246,11 +242,16 @@ void k_attn_bf16(AttnArgs a) {
         for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    // ---- per-lane byte offsets of the operand reads
+    // ---- per-lane LDS byte addresses of the operand reads in stage 0; other
+    // stages and sub-tiles add a constant that fits the 16-bit offset of the
+    // read (the V stages lie above 64 KB, so their base is in the register)
     // K (A operand of S^T = K Q^T): row lr of the 32-key sub-tile, d chunk 2st+hb
     int kofs[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) kofs[st] = 2 * (lr * kD + (((2 * st + hb) ^ (lr & 15)) << 3));
+    for (int st = 0; st < 8; ++st) {
+        kofs[st] = (int)lds_addr(kst<0>()) + 2 * (lr * kD + (((2 * st + hb) ^ (lr & 15)) << 3));
+        asm volatile("" : "+v"(kofs[st]));
+    }
     // V^T (A operand of O^T += V^T P^T) for dv block b: lane group g = lane/16
     // supplies keys 4hb + u/4 (+16jj, +8 for the upper half of the 16 keys) and
     // dims 32b + 16(g&1) + 4(u%4) .. +3 of the row-major tile; the transpose
@@ -263,16 +264,19 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int cidx = 4 * b + 2 * (g & 1) + ((u & 3) >> 1);
-            vofs[b] = r * (kD * 2) + ((cidx ^ (4 * (r & 3))) << 4) + 8 * (u & 1);
+            vofs[b] = (int)lds_addr(vst<0>()) + r * (kD * 2) + ((cidx ^ (4 * (r & 3))) << 4) + 8 * (u & 1);
+            asm volatile("" : "+v"(vofs[b]));
         }
     }
     auto read_k = [&](const uint16_t *kt, int sub, int st) __attribute__((always_inline)) -> bf16x8 {
-        return *(const WA_LDS bf16x8 *)((const WA_LDS char *)kt + sub * 32 * kD * 2 + kofs[st]);
+        return *(const WA_LDS bf16x8 *)((const WA_LDS char *)(uintptr_t)(unsigned)kofs[st] +
+                                        (lds_addr(kt) - lds_addr(kst<0>())) + sub * 32 * kD * 2);
     };
     // V^T operand `op` = 4 jj + b of sub-tile `sub`
     auto read_v = [&](const uint16_t *vt, int sub, int op) __attribute__((always_inline)) -> bf16x8 {
         const int jj = op >> 2, b = op & 3;
-        const WA_LDS char *base = (const WA_LDS char *)vt + (sub * 32 + 16 * jj) * kD * 2 + vofs[b];
+        const WA_LDS char *base = (const WA_LDS char *)(uintptr_t)(unsigned)vofs[b] +
+                                  (lds_addr(vt) - lds_addr(vst<0>())) + (sub * 32 + 16 * jj) * kD * 2;
         i16x4 half[2];
         half[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)base);
         half[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)(base + 8 * kD * 2));
@@ -285,12 +289,14 @@ void k_attn_bf16(AttnArgs a) {
     // loaded as copies of the last key, so maxima taken before masking are
     // still maxima over real keys; masking only has to precede the exponentials.
     auto mask_tail = [&](f32x16 &s, int key0) __attribute__((always_inline)) {
-        asm volatile("; mask tail" ::: "memory");
+        // element i holds key key0 + 8(i/4) + 4hb + i%4; the limit is made
+        // opaque so that the compares stay here instead of being hoisted out
+        // of the loop into 32 live scalar registers
+        int lim = n_keys - key0 - 4 * hb;
+        asm volatile("; mask tail" : "+v"(lim));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 8 * (i >> 2) + 4 * hb + (i & 3);
-            if (key >= n_keys) s[i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) >= lim) s[i] = -INFINITY;
     };
     // ---- move the reference max (and rescale the output) when it grew enough
     auto rescale = [&](float mt, bool live) __attribute__((always_inline)) {
@@ -357,13 +363,13 @@ void k_attn_bf16(AttnArgs a) {
 
     // ---- prologue: tiles 0, 1 and 2 in flight, wait for tile 0
     static_assert(2 * kCopies == 4, "the waits below count 4 copies per tile");
-    issue_tile(0, kst<0>(), vst<0>());
+    issue_tile(0, StageTag<0>{});
     if (n_tiles > 2) {
-        issue_tile(1, kst<1>(), vst<1>());
-        issue_tile(2, kst<2>(), vst<2>());
+        issue_tile(1, StageTag<1>{});
+        issue_tile(2, StageTag<2>{});
         wait_vm8();
     } else if (n_tiles > 1) {
-        issue_tile(1, kst<1>(), vst<1>());
+        issue_tile(1, StageTag<1>{});
         wait_vm4();
     } else {
         wait_vm0();
@@ -411,7 +417,7 @@ void k_attn_bf16(AttnArgs a) {
         else
             wait_vm0();
         __syncthreads();
-        if (t + 3 < n_tiles) issue_tile(t + 3, kst<S3>(), vst<S3>());
+        if (t + 3 < n_tiles) issue_tile(t + 3, StageTag<S3>{});
         pv_max(vst<S>(), 0, pa, av, sb, mtb, kst<S1>(), 0, ak);
         rescale(mtb, true);
         if (ragged && last) mask_tail(sb, t * kBN + 32);
