@@ -96,6 +96,8 @@ def main():
     idx = torch.empty(wl.k_p, dtype=torch.int32, device=dev)
     ws_sel = torch.empty(wa.wa_select_workspace_bytes(L, wl.n_q, wl.n_pages), dtype=torch.uint8,
                          device=dev)
+    ws_attn = torch.empty(max(16, wa.wa_attention_workspace_bytes(L, wl.n_q, wl.n_ctx, wl.n_q)),
+                          dtype=torch.uint8, device=dev)
     ctx_shape = (wl.n_ctx, wl.n_heads, wl.head_dim)
     k_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
     v_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
@@ -127,7 +129,7 @@ def main():
         if timed is not None:
             timed[3].record(stream)
         wa.wa_block_attention(L, q, k_ctx, v_ctx, k_own, v_own, wl.softmax_scale,
-                              out_dtype=wa.WA_BF16, out=out, stream=stream)
+                              out_dtype=wa.WA_BF16, out=out, workspace=ws_attn, stream=stream)
         if timed is not None:
             timed[4].record(stream)
 

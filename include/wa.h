@@ -199,16 +199,28 @@ wa_status wa_gather(const wa_layout *layout, const void *k_pool, const void *v_p
  * lse: device [H][n_q] float, or NULL.  n_ctx or n_own may be 0 (the
  * matching pointers may then be NULL).  out must not overlap any input.
  * page_tokens and max_pages of the layout are not used.
+ * workspace: device memory of at least wa_attention_workspace_bytes() bytes
+ * for the same arguments (16-byte aligned; may be NULL when that is 0),
+ * owned by the caller; it holds partial results of a launch that splits the
+ * key range of some (query block, head) items over several blocks so that
+ * every CU has work, and must not be shared by calls in flight at once.
  * Errors: NULL layout / q / out, NULL pointers of a non-empty segment,
  * n_q < 1, n_ctx < 0, n_own < 0, n_ctx + n_own < 1, non-finite
- * softmax_scale -> WA_ERR_INVALID_ARG; head_dim or out_dtype not supported
- * for the dtype -> WA_ERR_UNSUPPORTED.
+ * softmax_scale, workspace missing or too small -> WA_ERR_INVALID_ARG;
+ * head_dim or out_dtype not supported for the dtype -> WA_ERR_UNSUPPORTED.
  */
 wa_status wa_block_attention(const wa_layout *layout, const void *q, int32_t n_q,
                              const void *k_ctx, const void *v_ctx, int32_t n_ctx,
                              const void *k_own, const void *v_own, int32_t n_own,
                              float softmax_scale, int32_t out_dtype, void *out, float *lse,
-                             void *stream);
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace wa_block_attention needs for these arguments on the
+ * current device (0 for WA_F32 layouts and for launches that do not split;
+ * 0 for arguments wa_block_attention would reject).  A pure function of the
+ * arguments and the device's compute-unit count; launches nothing. */
+size_t wa_attention_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ctx,
+                                    int32_t n_own);
 
 /* Static text describing a status code. */
 const char *wa_status_string(wa_status status);

@@ -23,7 +23,8 @@ import torch
 __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "WA_F32", "WA_BF16",
            "Layout", "PromptStage", "WaError", "load_library", "library_path", "layout",
            "wa_append_workspace_bytes", "wa_append_page", "wa_select_workspace_bytes",
-           "wa_select_pages", "wa_gather", "wa_block_attention", "wa_status_string"]
+           "wa_select_pages", "wa_gather", "wa_attention_workspace_bytes", "wa_block_attention",
+           "wa_status_string"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -95,7 +96,9 @@ def load_library():
     lib.wa_select_pages.restype = i32
     lib.wa_gather.argtypes = [L, p, p, p, i32, p, p, p]
     lib.wa_gather.restype = i32
-    lib.wa_block_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, i32, p, p, p]
+    lib.wa_attention_workspace_bytes.argtypes = [L, i32, i32, i32]
+    lib.wa_attention_workspace_bytes.restype = sz
+    lib.wa_block_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, i32, p, p, p, sz, p]
     lib.wa_block_attention.restype = i32
     lib.wa_status_string.argtypes = [i32]
     lib.wa_status_string.restype = ctypes.c_char_p
@@ -264,8 +267,13 @@ def wa_gather(L: Layout, k_pool, v_pool, idx, k_p: int, k_ctx=None, v_ctx=None, 
     return k_ctx, v_ctx
 
 
+def wa_attention_workspace_bytes(L: Layout, n_q: int, n_ctx: int, n_own: int) -> int:
+    return int(load_library().wa_attention_workspace_bytes(ctypes.byref(L), int(n_q), int(n_ctx),
+                                                           int(n_own)))
+
+
 def wa_block_attention(L: Layout, q, k_ctx, v_ctx, k_own, v_own, softmax_scale=None,
-                       out_dtype=None, out=None, lse=None, stream=None):
+                       out_dtype=None, out=None, lse=None, workspace=None, stream=None):
     """Unmasked attention of q over [k_ctx ++ k_own]; returns out [n_q, H, d]."""
     lib = load_library()
     dt = L.torch_dtype
@@ -295,9 +303,11 @@ def wa_block_attention(L: Layout, q, k_ctx, v_ctx, k_own, v_own, softmax_scale=N
     _need(out, "out", odt, n_q * row)
     if lse is not None:
         _need(lse, "lse", torch.float32, n_q * L.n_heads)
+    nbytes = lib.wa_attention_workspace_bytes(ctypes.byref(L), int(n_q), int(n_ctx), int(n_own))
+    ws = _workspace(nbytes, workspace, q)
     st = lib.wa_block_attention(ctypes.byref(L), _ptr(q), int(n_q), _ptr(k_ctx), _ptr(v_ctx),
                                 int(n_ctx), _ptr(k_own), _ptr(v_own), int(n_own),
                                 float(softmax_scale), int(out_dtype), _ptr(out), _ptr(lse),
-                                _stream(stream))
+                                _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "wa_block_attention")
     return out

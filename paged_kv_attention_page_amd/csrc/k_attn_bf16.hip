@@ -57,6 +57,10 @@ static constexpr int kTileElems = kBN * kD;
 static constexpr int kRowsPerWave = kBN / kWaves;   // tile rows each wavefront copies
 static constexpr int kCopies = kRowsPerWave / 4;    // 1 KB copies per tensor per wavefront
 static constexpr float kRescaleLog2 = 8.f;   // rescale when the max grows by > 2^8
+static constexpr int kMaxSplitBlocks = 256;  // blocks of a split launch (partial slots)
+static constexpr int kMinSplitTiles = 16;    // fewest tiles per block worth a split
+static constexpr int kMaxBlocksPerItem = 32; // split blocks per (query block, head) item
+static constexpr int kMaxSlots = 64;         // pieces of one item a split may leave
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
     const int q = n >> 3, r = n & 7;
@@ -71,10 +75,47 @@ struct AttnArgs {
     const uint16_t *k_own;
     const uint16_t *v_own;
     int n_q, n_ctx, n_own, n_heads, q_blocks;
-    float c;        // softmax_scale * log2(e)
+    int n_tiles;        // 64-key tiles per item (T)
+    int split;          // 1: blocks take equal runs of the items' tiles
+    int grid;           // blocks of the attention launch (G)
+    int items;          // q_blocks * n_heads
+    int head_tiles;     // split: tiles [0, S) of each item form the first phase
+    int slots;          // split: partial slots per item
+    int64_t total;      // items * n_tiles
+    float c;            // softmax_scale * log2(e)
     int out_bf16;
     void *out;
     float *lse;
+    float *part_o;      // [items][slots][kBM][kD] unnormalised partial outputs
+    float *part_ml;     // [items][slots][kBM][2] reference max and row sum
+};
+
+// Work order of a split launch.  Position g in [0, items * T) names one 64-key
+// tile of one item: first tiles [0, S) of every item, item after item (phase
+// 0), then tiles [S, T) of every item (phase 1); block w takes positions
+// [w total / G, (w+1) total / G).  With S = total / G, block b < items spends
+// almost all its run on the first S tiles of item b, so the blocks of one head
+// stream the same K/V tiles at about the same time (one L2 per XCD serves
+// them), and the remaining blocks share out the tails.  Every piece of an
+// item that one block computes is one partial slot of that item.
+struct SplitMap {
+    int64_t total;
+    int grid, items, T, S;
+    __device__ explicit SplitMap(const AttnArgs &a)
+        : total(a.total), grid(a.grid), items(a.items), T(a.n_tiles), S(a.head_tiles) {}
+    __device__ int64_t bnd(int w) const { return (int64_t)w * total / grid; }
+    // the block whose run holds position x (the last one, past empty runs)
+    __device__ int block_of(int64_t x) const { return (int)(((x + 1) * grid - 1) / total); }
+    __device__ int64_t part_begin(int i, int p) const {
+        return p == 0 ? (int64_t)i * S : (int64_t)items * S + (int64_t)i * (T - S);
+    }
+    __device__ int64_t part_end(int i, int p) const { return part_begin(i, p) + (p == 0 ? S : T - S); }
+    // partial slot of the piece of part p of item i computed by block w
+    __device__ int slot(int i, int p, int w) const {
+        int base = 0;
+        if (p == 1 && S > 0) base = block_of(part_end(i, 0) - 1) - block_of(part_begin(i, 0)) + 1;
+        return base + (w - block_of(part_begin(i, p)));
+    }
 };
 
 // One 16-byte-per-lane DMA from global memory into LDS: lane i's 16 bytes
@@ -109,6 +150,17 @@ __device__ __forceinline__ T *sgpr_ptr(T *p) {
     uint64_t x = (uint64_t)(uintptr_t)p;
     asm volatile("" : "+s"(x));
     return (T *)(uintptr_t)x;
+}
+// A pointer that is the same in every lane, declared so (it derives from the
+// block index only, which the compiler cannot always see through loops).
+// readfirstlane returns a signed int: each half goes through unsigned before
+// it is widened, or a low half with bit 31 set would fill the high half.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t x = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)x);
+    const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+    return (T *)(uintptr_t)(lo | (hi << 32));
 }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
@@ -154,12 +206,12 @@ void k_attn_bf16(AttnArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, hb = lane >> 5;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = logical / a.q_blocks;
-    const int q0 = (logical % a.q_blocks) * kBM + wave * kWQ;
+    // consecutive logical blocks run on one XCD (one L2): with the split, they
+    // take consecutive runs of the same head's work
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t hd = (int64_t)a.n_heads * kD;
     const int n_keys = a.n_ctx + a.n_own;
-    const int n_tiles = (n_keys + kBN - 1) / kBN;
+    const int n_tiles = a.n_tiles;
     const bool ragged = (n_keys % kBN) != 0;
     const float c = a.c;
     const float thr = kRescaleLog2 / c;   // raw-score growth that forces a rescale
@@ -172,6 +224,58 @@ void k_attn_bf16(AttnArgs a) {
         __builtin_amdgcn_readfirstlane(lds_addr(lds_ring) + kRowsPerWave * wave * kD * 2);
     const uint16_t *const k_ctx = sgpr_ptr(a.k_ctx), *const v_ctx = sgpr_ptr(a.v_ctx);
     const uint16_t *const k_own = sgpr_ptr(a.k_own), *const v_own = sgpr_ptr(a.v_own);
+
+    // ---- per-lane LDS byte addresses of the operand reads in stage 0; other
+    // stages and sub-tiles add a constant that fits the 16-bit offset of the
+    // read (the V stages lie above 64 KB, so their base is in the register)
+    // K (A operand of S^T = K Q^T): row lr of the 32-key sub-tile, d chunk 2st+hb
+    int kofs[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        kofs[st] = (int)lds_addr(kst<0>()) + 2 * (lr * kD + (((2 * st + hb) ^ (lr & 15)) << 3));
+        asm volatile("" : "+v"(kofs[st]));
+    }
+    // V^T (A operand of O^T += V^T P^T) for dv block b: lane group g = lane/16
+    // supplies keys 4hb + u/4 (+16jj, +8 for the upper half of the 16 keys) and
+    // dims 32b + 16(g&1) + 4(u%4) .. +3 of the row-major tile; the transpose
+    // read hands lane 16g+i dim 32b+16(g&1)+i over those keys, in the key order
+    // of the S^T accumulator (keys 8(i/4) + 4hb + i%4 of each 16-key step).
+    int vofs[4];
+    {
+        const int u = lane & 15, g = lane >> 4;
+        const int r = 4 * hb + (u >> 2);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int cidx = 4 * b + 2 * (g & 1) + ((u & 3) >> 1);
+            vofs[b] = (int)lds_addr(vst<0>()) + r * (kD * 2) + ((cidx ^ (4 * (r & 3))) << 4) + 8 * (u & 1);
+            asm volatile("" : "+v"(vofs[b]));
+        }
+    }
+    auto read_k = [&](const uint16_t *kt, int sub, int st) __attribute__((always_inline)) -> bf16x8 {
+        return *(const WA_LDS bf16x8 *)((const WA_LDS char *)(uintptr_t)(unsigned)kofs[st] +
+                                        (lds_addr(kt) - lds_addr(kst<0>())) + sub * 32 * kD * 2);
+    };
+    // V^T operand `op` = 4 jj + b of sub-tile `sub`
+    auto read_v = [&](const uint16_t *vt, int sub, int op) __attribute__((always_inline)) -> bf16x8 {
+        const int jj = op >> 2, b = op & 3;
+        const WA_LDS char *base = (const WA_LDS char *)(uintptr_t)(unsigned)vofs[b] +
+                                  (lds_addr(vt) - lds_addr(vst<0>())) + (sub * 32 + 16 * jj) * kD * 2;
+        i16x4 half[2];
+        half[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)base);
+        half[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)(base + 8 * kD * 2));
+        bf16x8 av;
+        __builtin_memcpy(&av, half, sizeof(av));
+        return av;
+    };
+
+  // One segment: tiles [t_begin, t_end) of item `item` (query block
+  // item % q_blocks of head item / q_blocks).  Without the split a segment is
+  // a whole item, normalised and written out; with it, a piece leaves its
+  // unnormalised output, reference max and row sum in partial slot `slot` of
+  // the item.
+  auto segment = [&](int item, int t_begin, int t_end, int slot) __attribute__((always_inline)) {
+    const int h = item / a.q_blocks;
+    const int q0 = (item % a.q_blocks) * kBM + wave * kWQ;
     // per-lane byte offsets of this lane's 16 bytes within a tile whose first
     // row is at a uniform base (fast path: the tile lies inside one segment)
     unsigned koff[kCopies], voff[kCopies];
@@ -197,6 +301,8 @@ void k_attn_bf16(AttnArgs a) {
             vb = v_own + (int64_t)(key0 - a.n_ctx) * hd;
         }
         if (kb) {
+            kb = uniform_ptr(kb);
+            vb = uniform_ptr(vb);
             dma16_sbase<OK>(kb, koff[0], ld_base);
             dma16_sbase<OV>(vb, voff[0], ld_base);
             dma16_sbase<OK + ROWS4>(kb, koff[1], ld_base);
@@ -241,49 +347,6 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
     float m = -INFINITY, l = 0.f;
-
-    // ---- per-lane LDS byte addresses of the operand reads in stage 0; other
-    // stages and sub-tiles add a constant that fits the 16-bit offset of the
-    // read (the V stages lie above 64 KB, so their base is in the register)
-    // K (A operand of S^T = K Q^T): row lr of the 32-key sub-tile, d chunk 2st+hb
-    int kofs[8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-        kofs[st] = (int)lds_addr(kst<0>()) + 2 * (lr * kD + (((2 * st + hb) ^ (lr & 15)) << 3));
-        asm volatile("" : "+v"(kofs[st]));
-    }
-    // V^T (A operand of O^T += V^T P^T) for dv block b: lane group g = lane/16
-    // supplies keys 4hb + u/4 (+16jj, +8 for the upper half of the 16 keys) and
-    // dims 32b + 16(g&1) + 4(u%4) .. +3 of the row-major tile; the transpose
-    // read hands lane 16g+i dim 32b+16(g&1)+i over those keys, in the key order
-    // of the S^T accumulator (keys 8(i/4) + 4hb + i%4 of each 16-key step).
-    int vofs[4];
-    {
-        const int u = lane & 15, g = lane >> 4;
-        const int r = 4 * hb + (u >> 2);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int cidx = 4 * b + 2 * (g & 1) + ((u & 3) >> 1);
-            vofs[b] = (int)lds_addr(vst<0>()) + r * (kD * 2) + ((cidx ^ (4 * (r & 3))) << 4) + 8 * (u & 1);
-            asm volatile("" : "+v"(vofs[b]));
-        }
-    }
-    auto read_k = [&](const uint16_t *kt, int sub, int st) __attribute__((always_inline)) -> bf16x8 {
-        return *(const WA_LDS bf16x8 *)((const WA_LDS char *)(uintptr_t)(unsigned)kofs[st] +
-                                        (lds_addr(kt) - lds_addr(kst<0>())) + sub * 32 * kD * 2);
-    };
-    // V^T operand `op` = 4 jj + b of sub-tile `sub`
-    auto read_v = [&](const uint16_t *vt, int sub, int op) __attribute__((always_inline)) -> bf16x8 {
-        const int jj = op >> 2, b = op & 3;
-        const WA_LDS char *base = (const WA_LDS char *)(uintptr_t)(unsigned)vofs[b] +
-                                  (lds_addr(vt) - lds_addr(vst<0>())) + (sub * 32 + 16 * jj) * kD * 2;
-        i16x4 half[2];
-        half[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)base);
-        half[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)(base + 8 * kD * 2));
-        bf16x8 av;
-        __builtin_memcpy(&av, half, sizeof(av));
-        return av;
-    };
 
     // ---- keys past the end (last tile only) get score -inf.  Their rows were
     // loaded as copies of the last key, so maxima taken before masking are
@@ -361,15 +424,17 @@ void k_attn_bf16(AttnArgs a) {
         mt = xhalf_max(x);
     };
 
-    // ---- prologue: tiles 0, 1 and 2 in flight, wait for tile 0
+    // ---- prologue: every wave is past its reads of the previous segment's
+    // tiles; tiles t_begin .. t_begin+2 in flight, wait for t_begin
     static_assert(2 * kCopies == 4, "the waits below count 4 copies per tile");
-    issue_tile(0, StageTag<0>{});
-    if (n_tiles > 2) {
-        issue_tile(1, StageTag<1>{});
-        issue_tile(2, StageTag<2>{});
+    __syncthreads();
+    issue_tile(t_begin, StageTag<0>{});
+    if (t_end - t_begin > 2) {
+        issue_tile(t_begin + 1, StageTag<1>{});
+        issue_tile(t_begin + 2, StageTag<2>{});
         wait_vm8();
-    } else if (n_tiles > 1) {
-        issue_tile(1, StageTag<1>{});
+    } else if (t_end - t_begin > 1) {
+        issue_tile(t_begin + 1, StageTag<1>{});
         wait_vm4();
     } else {
         wait_vm0();
@@ -393,7 +458,7 @@ void k_attn_bf16(AttnArgs a) {
         for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[i]);
         mta = xhalf_max(x);
         rescale(mta, true);
-        if (ragged && n_tiles == 1) mask_tail(sa, 0);
+        if (ragged && t_begin == n_tiles - 1) mask_tail(sa, t_begin * kBN);
         ak[0] = read_k(kst<0>(), 1, 0);
         ak[1] = read_k(kst<0>(), 1, 1);
     }
@@ -407,27 +472,27 @@ void k_attn_bf16(AttnArgs a) {
     auto tile = [&](int t, auto stage_tag) __attribute__((always_inline)) -> bool {
         constexpr int S = decltype(stage_tag)::value;
         constexpr int S1 = (S + 1) % kStages, S3 = (S + 3) % kStages;
-        const bool last = t == n_tiles - 1;
+        const bool last = t == t_end - 1;
         qk_softmax(kst<S>(), 1, sb, sa, pa, ak, vst<S>(), 0, av);
         // tile t+1 must be in LDS for every wave (tile t+2 may still be in
         // flight), and every wave is past its reads of tile t-1, whose stage
         // is refilled
-        if (t + 2 < n_tiles)
+        if (t + 2 < t_end)
             wait_vm4();
         else
             wait_vm0();
         __syncthreads();
-        if (t + 3 < n_tiles) issue_tile(t + 3, StageTag<S3>{});
+        if (t + 3 < t_end) issue_tile(t + 3, StageTag<S3>{});
         pv_max(vst<S>(), 0, pa, av, sb, mtb, kst<S1>(), 0, ak);
         rescale(mtb, true);
-        if (ragged && last) mask_tail(sb, t * kBN + 32);
+        if (ragged && t == n_tiles - 1) mask_tail(sb, t * kBN + 32);
         qk_softmax(kst<S1>(), 0, sa, sb, pbk, ak, vst<S>(), 1, av);
         pv_max(vst<S>(), 1, pbk, av, sa, mta, kst<S1>(), 1, ak);
         rescale(mta, !last);
-        if (ragged && t + 1 == n_tiles - 1) mask_tail(sa, (t + 1) * kBN);
+        if (ragged && t + 1 == n_tiles - 1 && !last) mask_tail(sa, (t + 1) * kBN);
         return last;
     };
-    for (int t = 0;; t += 4) {
+    for (int t = t_begin;; t += 4) {
         if (tile(t, StageTag<0>{})) break;
         if (tile(t + 1, StageTag<1>{})) break;
         if (tile(t + 2, StageTag<2>{})) break;
@@ -436,6 +501,19 @@ void k_attn_bf16(AttnArgs a) {
 
     // ---- epilogue: O^T[dv][q] / l; lanes l and l^32 hold halves of l
     const float lt = xhalf_sum(l);
+    if (a.split) {
+        // piece of an item: unnormalised output, reference max, row sum
+        const int64_t prow = ((int64_t)item * a.slots + slot) * kBM + wave * kWQ + lr;
+        float *po = a.part_o + prow * kD;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(float4 *)(po + 32 * b + 8 * g + 4 * hb) =
+                    make_float4(o[b][4 * g], o[b][4 * g + 1], o[b][4 * g + 2], o[b][4 * g + 3]);
+        if (hb == 0) *(float2 *)(a.part_ml + 2 * prow) = make_float2(m, lt);
+        return;
+    }
     const float inv = 1.f / lt;
     const int row = q0 + lr;
     if (row < a.n_q) {
@@ -458,13 +536,136 @@ void k_attn_bf16(AttnArgs a) {
         if (a.lse && hb == 0)
             a.lse[(int64_t)h * a.n_q + row] = (m * c + __log2f(lt)) * 0.69314718055994531f;
     }
+  };
+
+    // ---- this block's work: one whole item, or (split) its run of positions
+    if (!a.split) {
+        segment(blk, 0, n_tiles, 0);
+        return;
+    }
+    const SplitMap map(a);
+    const int64_t g1 = map.bnd(blk + 1), phase0 = (int64_t)a.items * map.S;
+    for (int64_t g = map.bnd(blk); g < g1;) {
+        int item, part, t_begin;
+        if (g < phase0) {
+            part = 0;
+            item = (int)(g / map.S);
+            t_begin = (int)(g - (int64_t)item * map.S);
+        } else {
+            part = 1;
+            const int64_t h1 = g - phase0;
+            item = (int)(h1 / (n_tiles - map.S));
+            t_begin = map.S + (int)(h1 - (int64_t)item * (n_tiles - map.S));
+        }
+        const int64_t pend = map.part_end(item, part);
+        const int64_t gend = pend < g1 ? pend : g1;
+        const int t_end = t_begin + (int)(gend - g);
+        segment(__builtin_amdgcn_readfirstlane(item), __builtin_amdgcn_readfirstlane(t_begin),
+                __builtin_amdgcn_readfirstlane(t_end), map.slot(item, part, blk));
+        g = gend;
+    }
+}
+
+// Merge the pieces of every item of a split launch: for each query row,
+// M = max of the reference maxima, L = sum l_j 2^{c(m_j - M)},
+// O = sum O_j 2^{c(m_j - M)} / L, pieces in slot order (a running maximum
+// with rescaling, so all the pieces' loads are independent).  One block of
+// 256 threads per 8 query rows of an item: lane group (wave, lane / 32) owns
+// a row, 32 lanes x 4 dims cover its 128 dims.
+static constexpr int kMergeRows = 8;
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+    __shared__ int slot_list[kMaxSlots];
+    __shared__ int n_pieces;
+    const int item = blockIdx.x / (kBM / kMergeRows);
+    const int r = (blockIdx.x % (kBM / kMergeRows)) * kMergeRows + (threadIdx.x >> 5);
+    if (threadIdx.x == 0) {
+        const SplitMap map(a);
+        int n = 0;
+        for (int p = 0; p < 2; ++p) {
+            const int64_t b = map.part_begin(item, p), e = map.part_end(item, p);
+            if (b >= e) continue;
+            for (int w = map.block_of(b), wl = map.block_of(e - 1); w <= wl; ++w)
+                if (map.bnd(w + 1) > map.bnd(w) && n < kMaxSlots) slot_list[n++] = map.slot(item, p, w);
+        }
+        n_pieces = n;
+    }
+    __syncthreads();
+    const int np = n_pieces;
+    const int h = item / a.q_blocks, qb = item % a.q_blocks;
+    const int row = qb * kBM + r;
+    if (row >= a.n_q) return;
+    const int64_t hd = (int64_t)a.n_heads * kD;
+    const float c = a.c;
+    const int d = 4 * (threadIdx.x & 31);
+    const int64_t row0 = (int64_t)item * a.slots * kBM + r;
+    float M = -INFINITY, L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < np; ++j) {
+        const int64_t pr = row0 + (int64_t)slot_list[j] * kBM;
+        const float2 ml = *(const float2 *)(a.part_ml + 2 * pr);
+        const float4 v = *(const float4 *)(a.part_o + pr * kD + d);
+        const float mn = fmaxf(M, ml.x);
+        const float fo = __builtin_amdgcn_exp2f((M - mn) * c);   // 0 on the first piece
+        const float f = __builtin_amdgcn_exp2f((ml.x - mn) * c);
+        L = L * fo + ml.y * f;
+        acc.x = acc.x * fo + v.x * f;
+        acc.y = acc.y * fo + v.y * f;
+        acc.z = acc.z * fo + v.z * f;
+        acc.w = acc.w * fo + v.w * f;
+        M = mn;
+    }
+    const float inv = 1.f / L;
+    const int64_t base = (int64_t)row * hd + h * kD + d;
+    if (a.out_bf16) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv),
+                    (__bf16)(acc.w * inv)};
+        *(bf16x4 *)((uint16_t *)a.out + base) = v;
+    } else {
+        *(float4 *)((float *)a.out + base) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (a.lse && d == 0)
+        a.lse[(int64_t)h * a.n_q + row] = (M * c + __log2f(L)) * 0.69314718055994531f;
+}
+
+AttnPlan attention_plan(int32_t n_heads, int32_t n_q, int32_t n_keys, int cu_count) {
+    AttnPlan p;
+    const int q_blocks = (n_q + kBM - 1) / kBM;
+    const int items = q_blocks * n_heads;
+    p.n_tiles = (n_keys + kBN - 1) / kBN;
+    p.total = (int64_t)items * p.n_tiles;
+    p.items = items;
+    int g = cu_count < kMaxSplitBlocks ? cu_count : kMaxSplitBlocks;
+    if ((int64_t)items * kMaxBlocksPerItem < g) g = items * kMaxBlocksPerItem;
+    // split when one block per item would leave more than a quarter of the
+    // CUs idle, and each block still gets a long run of tiles.  (With 89 % of
+    // the CUs busy the split measured no faster: under a full matrix-core
+    // load the clock falls as more CUs draw power, and the merge costs 1-2 %.)
+    p.split = (int64_t)items * 4 <= (int64_t)g * 3 && p.total / g >= kMinSplitTiles;
+    p.grid = p.split ? g : items;
+    p.head_tiles = p.split ? (int)(p.total / g) : 0;
+    p.slots = 0;
+    if (p.split) {
+        // pieces per item: a part of length n meets at most ceil(n / run) + 1
+        // runs, runs being at least total / G = S long
+        const int64_t run = p.total / g, tail = p.n_tiles - p.head_tiles;
+        p.slots = (p.head_tiles > 0 ? 2 : 0) + (int)((tail + run - 1) / run) + 1;
+        if (p.slots > kMaxSlots) {   // cannot happen with at most 32 blocks per item
+            p.split = 0;
+            p.grid = items;
+            p.head_tiles = p.slots = 0;
+        }
+    }
+    p.workspace = (size_t)items * p.slots * kBM * (kD + 2) * sizeof(float);
+    return p;
 }
 
 hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q,
                                  const uint16_t *k_ctx, const uint16_t *v_ctx, int32_t n_ctx,
                                  const uint16_t *k_own, const uint16_t *v_own, int32_t n_own,
                                  float scale, int32_t out_dtype, void *out, float *lse,
-                                 hipStream_t s) {
+                                 const AttnPlan &plan, void *workspace, hipStream_t s) {
     AttnArgs a;
     a.q = q;
     a.k_ctx = k_ctx;
@@ -476,12 +677,24 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
     a.n_own = n_own;
     a.n_heads = n_heads;
     a.q_blocks = (n_q + kBM - 1) / kBM;
+    a.n_tiles = plan.n_tiles;
+    a.split = plan.split;
+    a.grid = plan.grid;
+    a.items = plan.items;
+    a.head_tiles = plan.head_tiles;
+    a.slots = plan.slots;
+    a.total = plan.total;
     a.c = scale * 1.4426950408889634f;
     a.out_bf16 = out_dtype == WA_BF16;
     a.out = out;
     a.lse = lse;
-    const unsigned grid = (unsigned)(a.q_blocks * n_heads);
-    hipLaunchKernelGGL(k_attn_bf16, dim3(grid), dim3(kThreads), 0, s, a);
+    a.part_o = plan.split ? (float *)workspace : nullptr;
+    a.part_ml = plan.split ? (float *)workspace + (size_t)plan.items * plan.slots * kBM * kD : nullptr;
+    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)plan.grid), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !plan.split) return e;
+    hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(a.q_blocks * n_heads * (kBM / kMergeRows))),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -111,10 +111,30 @@ wa_status wa_gather(const wa_layout *L, const void *k_pool, const void *v_pool, 
     return from_hip(launch_gather(*L, k_pool, v_pool, idx, k_p, k_ctx, v_ctx, (hipStream_t)stream));
 }
 
+// CUs of the current device; 256 (MI355X) when no device can be queried, so
+// that the workspace size can be asked for without a GPU.
+static int current_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return 256;
+    return n;
+}
+
+size_t wa_attention_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_ctx,
+                                    int32_t n_own) {
+    if (check_layout(L, false) != WA_OK || L->dtype != WA_BF16) return 0;
+    if (n_q < 1 || n_ctx < 0 || n_own < 0 || (int64_t)n_ctx + n_own < 1) return 0;
+    if ((int64_t)n_ctx + n_own > 0x7fffffff - 256) return 0;
+    return attention_plan(L->n_heads, n_q, n_ctx + n_own, current_cu_count()).workspace;
+}
+
 wa_status wa_block_attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
                              const void *v_ctx, int32_t n_ctx, const void *k_own,
                              const void *v_own, int32_t n_own, float softmax_scale,
-                             int32_t out_dtype, void *out, float *lse, void *stream) {
+                             int32_t out_dtype, void *out, float *lse, void *workspace,
+                             size_t ws_bytes, void *stream) {
     wa_status st = check_layout(L, false);
     if (st != WA_OK) return st;
     if (!q || !out) return WA_ERR_INVALID_ARG;
@@ -136,10 +156,14 @@ wa_status wa_block_attention(const wa_layout *L, const void *q, int32_t n_q, con
     }
     if (L->head_dim != 128) return WA_ERR_UNSUPPORTED;
     if (out_dtype != WA_F32 && out_dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
+    const AttnPlan plan = attention_plan(L->n_heads, n_q, n_ctx + n_own, current_cu_count());
+    if (plan.workspace > 0 && (!workspace || ws_bytes < plan.workspace || !aligned16(workspace)))
+        return WA_ERR_INVALID_ARG;
     return from_hip(launch_attention_bf16(L->n_heads, (const uint16_t *)q, n_q,
                                           (const uint16_t *)k_ctx, (const uint16_t *)v_ctx, n_ctx,
                                           (const uint16_t *)k_own, (const uint16_t *)v_own, n_own,
-                                          softmax_scale, out_dtype, out, lse, (hipStream_t)stream));
+                                          softmax_scale, out_dtype, out, lse, plan, workspace,
+                                          (hipStream_t)stream));
 }
 
 const char *wa_status_string(wa_status s) {

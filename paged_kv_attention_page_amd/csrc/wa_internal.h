@@ -74,10 +74,25 @@ hipError_t launch_attention_f32(int32_t n_heads, int32_t head_dim, const float *
                                 const float *k_own, const float *v_own, int32_t n_own,
                                 float scale, float *out, float *lse, hipStream_t s);
 
+// bf16 attention launch plan: one block per (query block, head) item, or
+// (split) one block per CU, each taking an equal run of the items' key tiles,
+// followed by a merge of the items shared by several blocks.
+struct AttnPlan {
+    int split;
+    int grid;
+    int items;
+    int n_tiles;
+    int head_tiles;     // split: first-phase tiles per item
+    int slots;          // split: partial slots per item
+    int64_t total;
+    size_t workspace;   // bytes of partial results (0 unless split)
+};
+AttnPlan attention_plan(int32_t n_heads, int32_t n_q, int32_t n_keys, int cu_count);
+
 hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q,
                                  const uint16_t *k_ctx, const uint16_t *v_ctx, int32_t n_ctx,
                                  const uint16_t *k_own, const uint16_t *v_own, int32_t n_own,
                                  float scale, int32_t out_dtype, void *out, float *lse,
-                                 hipStream_t s);
+                                 const AttnPlan &plan, void *workspace, hipStream_t s);
 
 }  // namespace wa

@@ -193,9 +193,26 @@ def test_gather_rejects(lib):
 # attention
 
 def _attn(lib, lay=None, q=A, n_q=64, kc=A, vc=B, n_ctx=64, ko=A, vo=B, n_own=64, scale=0.1,
-          odt=wa.WA_F32, out=B, lse=NULL):
+          odt=wa.WA_F32, out=B, lse=NULL, ws=NULL, ws_bytes=0):
     return lib.wa_block_attention(lay if lay is not None else L(), q, n_q, kc, vc, n_ctx, ko, vo,
-                                  n_own, scale, odt, out, lse, None)
+                                  n_own, scale, odt, out, lse, ws, ws_bytes, None)
+
+
+def test_attention_workspace_size(lib):
+    """A launch splits its items' key tiles over the CUs (256 on MI355X, and
+    when no device can be queried) only when one block per (query block, head)
+    item would leave more than a quarter of them idle.  The workspace then
+    holds one slot per piece an item was cut into: 256 x 128 fp32 outputs plus
+    a max and a row sum per query row.  4 query blocks x 12 heads x 318 tiles
+    on 256 blocks: 59 head tiles per item (at most 2 pieces), a 259-tile tail
+    (at most ceil(259 / 59) + 1 = 6 pieces)."""
+    assert lib.wa_attention_workspace_bytes(L(), 4680, 49920, 4680) == 0   # 228 items: no split
+    n = lib.wa_attention_workspace_bytes(L(), 1024, 20000, 300)
+    assert n == 48 * 8 * 256 * (128 + 2) * 4
+    assert lib.wa_attention_workspace_bytes(L(), 64, 64, 64) == 0          # too few tiles
+    assert lib.wa_attention_workspace_bytes(L(dtype=wa.WA_F32, d=64), 1024, 20000, 300) == 0
+    assert lib.wa_attention_workspace_bytes(L(), 0, 64, 64) == 0           # rejected arguments
+    assert lib.wa_attention_workspace_bytes(None, 64, 64, 64) == 0
 
 
 def test_attention_rejects(lib):
@@ -218,3 +235,7 @@ def test_attention_rejects(lib):
     assert _attn(lib, lay=L(dtype=wa.WA_F32, d=96)) == U       # fp32: 64 or 128
     assert _attn(lib, lay=L(dtype=wa.WA_F32, d=64), odt=wa.WA_BF16) == U
     assert _attn(lib, odt=5) == U
+    big = dict(n_q=1024, n_ctx=20000, n_own=300, odt=wa.WA_BF16)
+    assert _attn(lib, **big) == E                                         # workspace missing
+    assert _attn(lib, ws=A, ws_bytes=1024, **big) == E                    # too small
+    assert _attn(lib, ws=MIS, ws_bytes=1 << 30, **big) == E               # misaligned

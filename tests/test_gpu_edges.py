@@ -61,6 +61,27 @@ def test_attention_shapes(wl, n_q, n_ctx, n_own):
     assert np.abs(lse.cpu().double().numpy() - ref_lse).max() <= tol
 
 
+@pytest.mark.parametrize("odt", [wa.WA_F32, wa.WA_BF16], ids=["f32_out", "bf16_out"])
+def test_attention_split_over_cus(odt):
+    """Few (query block, head) items and many keys: the launch splits each
+    item's 630 key tiles into up to 36 pieces over 192 blocks and merges them.
+    Sampled rows of both query blocks against the oracle, lse included."""
+    wl = BF
+    n_q, n_ctx, n_own = 257, 40000, 257
+    L = wa_layout(wl)
+    assert wa.wa_attention_workspace_bytes(L, n_q, n_ctx, n_own) > 0, "expected a split launch"
+    q = rand_rows(wl, n_q, 11)
+    kc, vc = rand_rows(wl, n_ctx, 12), rand_rows(wl, n_ctx, 13)
+    ko, vo = rand_rows(wl, n_own, 14), rand_rows(wl, n_own, 15)
+    say("attention split", n_q, n_ctx, n_own, odt)
+    out, lse = attend(wl, q, kc, vc, ko, vo, odt=odt, lse=True)
+    rows = np.array([0, 1, 31, 32, 100, 200, 254, 255, 256], dtype=np.int64)
+    ref, ref_lse = oracle.attention(q, kc, vc, ko, vo, wl.softmax_scale, rows=rows)
+    got = to_f64(out)[rows]
+    assert np.abs(got - ref).max() <= 1e-2
+    assert np.abs(lse.cpu().double().numpy()[:, rows] - ref_lse).max() <= 1e-2
+
+
 def test_attention_unit_values_and_reruns_are_bitwise_equal():
     wl = BF
     q, kc, ko = rand_rows(wl, 200, 1), rand_rows(wl, 300, 2), rand_rows(wl, 70, 4)
