@@ -124,13 +124,14 @@ struct SplitMap {
 // inline assembly so that the compiler does not insert its own (conservative)
 // waits for the copy before unrelated LDS reads; the kernel waits for the
 // copies itself (vmcnt) before the barrier that publishes a tile.  Nothing
-// else in the kernel uses m0.
+// else in the kernel uses m0.  The scalar add writes SCC, so SCC is declared
+// clobbered: the compiler must not keep a carry live across the copy.
 template <unsigned OFF>
 __device__ __forceinline__ void dma16(const void *gptr, unsigned lds_base) {
     asm volatile("s_add_u32 m0, %0, %2\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_base), "v"(gptr), "i"(OFF)
-                 : "memory", "m0");
+                 : "memory", "m0", "scc");
 }
 // The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset: the per-lane offsets of a tile never change, so issuing a tile
@@ -140,7 +141,7 @@ __device__ __forceinline__ void dma16_sbase(const void *sbase, unsigned voff, un
     asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(lds_base), "v"(voff), "s"(sbase), "i"(OFF)
-                 : "memory", "m0");
+                 : "memory", "m0", "scc");
 }
 // A wave-uniform pointer kept in SGPRs: the empty asm makes the value opaque,
 // so the compiler cannot re-load it from the kernel arguments (with a wait on
@@ -183,6 +184,8 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // tiles.  Every access names its stage at compile time, so each address is a
 // per-lane (or wave-uniform) base plus a constant.
 static constexpr unsigned kTileBytes = kTileElems * 2;
+static constexpr int kStageBytes = kTileElems * 2;   // one K or V tile
+static constexpr int kSubBytes = 32 * kD * 2;        // one 32-key sub-tile
 __shared__ __attribute__((aligned(1024))) uint16_t lds_ring[2 * kStages * kTileElems];
 
 template <int S>
@@ -224,6 +227,18 @@ void k_attn_bf16(AttnArgs a) {
         __builtin_amdgcn_readfirstlane(lds_addr(lds_ring) + kRowsPerWave * wave * kD * 2);
     const uint16_t *const k_ctx = sgpr_ptr(a.k_ctx), *const v_ctx = sgpr_ptr(a.v_ctx);
     const uint16_t *const k_own = sgpr_ptr(a.k_own), *const v_own = sgpr_ptr(a.v_own);
+    // DMA sources: tile t holds keys [64t, 64t + 64).  It lies inside one
+    // segment unless it straddles n_ctx (t == t_mid) or passes the end
+    // (t >= t_full); inside one, its first row is base + t * tile_bytes, where
+    // the own segment's base is shifted back by the n_ctx keys before it.
+    const int t_ctx = a.n_ctx / kBN;
+    const int t_mid = (a.n_ctx % kBN) != 0 ? t_ctx : -1;
+    const int t_full = n_keys / kBN;
+    const uint32_t tile_bytes = (uint32_t)(kBN * hd * 2);
+    const uint64_t ctx_shift = (uint64_t)a.n_ctx * (uint64_t)hd * 2u;
+    const uint64_t kb_ctx = (uint64_t)(uintptr_t)k_ctx, vb_ctx = (uint64_t)(uintptr_t)v_ctx;
+    const uint64_t kb_own = (uint64_t)(uintptr_t)k_own - ctx_shift;
+    const uint64_t vb_own = (uint64_t)(uintptr_t)v_own - ctx_shift;
 
     // ---- per-lane LDS byte addresses of the operand reads in stage 0; other
     // stages and sub-tiles add a constant that fits the 16-bit offset of the
@@ -251,15 +266,17 @@ void k_attn_bf16(AttnArgs a) {
             asm volatile("" : "+v"(vofs[b]));
         }
     }
-    auto read_k = [&](const uint16_t *kt, int sub, int st) __attribute__((always_inline)) -> bf16x8 {
-        return *(const WA_LDS bf16x8 *)((const WA_LDS char *)(uintptr_t)(unsigned)kofs[st] +
-                                        (lds_addr(kt) - lds_addr(kst<0>())) + sub * 32 * kD * 2);
+    // `off` = ring byte offset of a (stage, sub-tile) within the K or the V
+    // tiles, kStageBytes * stage + kSubBytes * sub: a compile-time constant in
+    // every call, so it lands in the 16-bit offset of the read
+    auto read_k = [&](int off, int st) __attribute__((always_inline)) -> bf16x8 {
+        return *(const WA_LDS bf16x8 *)((const WA_LDS char *)(uintptr_t)(unsigned)kofs[st] + off);
     };
-    // V^T operand `op` = 4 jj + b of sub-tile `sub`
-    auto read_v = [&](const uint16_t *vt, int sub, int op) __attribute__((always_inline)) -> bf16x8 {
+    // V^T operand `op` = 4 jj + b of the sub-tile at `off`
+    auto read_v = [&](int off, int op) __attribute__((always_inline)) -> bf16x8 {
         const int jj = op >> 2, b = op & 3;
-        const WA_LDS char *base = (const WA_LDS char *)(uintptr_t)(unsigned)vofs[b] +
-                                  (lds_addr(vt) - lds_addr(vst<0>())) + (sub * 32 + 16 * jj) * kD * 2;
+        const WA_LDS char *base =
+            (const WA_LDS char *)(uintptr_t)(unsigned)vofs[b] + off + 16 * jj * kD * 2;
         i16x4 half[2];
         half[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)base);
         half[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WA_LDS i16x4 *)(base + 8 * kD * 2));
@@ -292,17 +309,11 @@ void k_attn_bf16(AttnArgs a) {
         constexpr unsigned OK = S * kTileBytes, OV = (kStages + S) * kTileBytes;
         constexpr unsigned ROWS4 = 4 * kD * 2;    // four tile rows
         const int key0 = t * kBN;
-        const uint16_t *kb = nullptr, *vb = nullptr;
-        if (key0 + kBN <= a.n_ctx) {
-            kb = k_ctx + (int64_t)key0 * hd;
-            vb = v_ctx + (int64_t)key0 * hd;
-        } else if (key0 >= a.n_ctx && key0 + kBN <= n_keys) {
-            kb = k_own + (int64_t)(key0 - a.n_ctx) * hd;
-            vb = v_own + (int64_t)(key0 - a.n_ctx) * hd;
-        }
-        if (kb) {
-            kb = uniform_ptr(kb);
-            vb = uniform_ptr(vb);
+        if (t != t_mid && t < t_full) {
+            const uint64_t off = (uint64_t)(uint32_t)t * tile_bytes;
+            const bool in_ctx = t < t_ctx;
+            const uint16_t *kb = uniform_ptr((const uint16_t *)(uintptr_t)((in_ctx ? kb_ctx : kb_own) + off));
+            const uint16_t *vb = uniform_ptr((const uint16_t *)(uintptr_t)((in_ctx ? vb_ctx : vb_own) + off));
             dma16_sbase<OK>(kb, koff[0], ld_base);
             dma16_sbase<OV>(vb, voff[0], ld_base);
             dma16_sbase<OK + ROWS4>(kb, koff[1], ld_base);
@@ -384,9 +395,8 @@ void k_attn_bf16(AttnArgs a) {
     // the P V products, l accumulated from the bf16 values.  ak[0], ak[1]
     // arrive prefetched; the V^T operands 0 and 1 of the following P V region
     // (sub-tile vsub of vt) are prefetched at the end.
-    auto qk_softmax = [&](const uint16_t *kt, int sub, f32x16 &sn, const f32x16 &sc,
-                          bf16x8 (&pb)[2], bf16x8 (&ak)[8], const uint16_t *vt, int vsub,
-                          bf16x8 (&av)[8]) __attribute__((always_inline)) {
+    auto qk_softmax = [&](int koff, f32x16 &sn, const f32x16 &sc, bf16x8 (&pb)[2],
+                          bf16x8 (&ak)[8], int voff, bf16x8 (&av)[8]) __attribute__((always_inline)) {
         const float mc = m * c;
         float ls = l;
         const f32x16 zero = {};
@@ -400,8 +410,8 @@ void k_attn_bf16(AttnArgs a) {
             pb[st >> 2][2 * (st & 3)] = pr[0];
             pb[st >> 2][2 * (st & 3) + 1] = pr[1];
             ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls, false);
-            if (st + 2 < 8) ak[st + 2] = read_k(kt, sub, st + 2);
-            if (st >= 6) av[st - 6] = read_v(vt, vsub, st - 6);
+            if (st + 2 < 8) ak[st + 2] = read_k(koff, st + 2);
+            if (st >= 6) av[st - 6] = read_v(voff, st - 6);
         }
         l = ls;
     };
@@ -409,17 +419,16 @@ void k_attn_bf16(AttnArgs a) {
     // ---- fused region PV+MAX: O^T += V^T P^T (8 MFMAs) interleaved with the
     // max of sn per query; prefetches the next V^T operands two steps ahead and,
     // at the end, the first two K operands of the next QK+SOFTMAX region.
-    auto pv_max = [&](const uint16_t *vt, int sub, const bf16x8 (&pb)[2], bf16x8 (&av)[8],
-                      const f32x16 &sn, float &mt, const uint16_t *kt_next, int ksub_next,
-                      bf16x8 (&ak)[8]) __attribute__((always_inline)) {
+    auto pv_max = [&](int voff, const bf16x8 (&pb)[2], bf16x8 (&av)[8], const f32x16 &sn,
+                      float &mt, int koff_next, bf16x8 (&ak)[8]) __attribute__((always_inline)) {
         float x = fmaxf(sn[0], sn[1]);
 #pragma unroll
         for (int op = 0; op < 8; ++op) {
             const int jj = op >> 2, b = op & 3;
             o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[op], pb[jj], o[b], 0, 0, 0);
             if (op < 7) x = fmaxf(x, fmaxf(sn[2 + 2 * op], sn[3 + 2 * op]));
-            if (op + 2 < 8) av[op + 2] = read_v(vt, sub, op + 2);
-            if (op >= 6) ak[op - 6] = read_k(kt_next, ksub_next, op - 6);
+            if (op + 2 < 8) av[op + 2] = read_v(voff, op + 2);
+            if (op >= 6) ak[op - 6] = read_k(koff_next, op - 6);
         }
         mt = xhalf_max(x);
     };
@@ -448,7 +457,7 @@ void k_attn_bf16(AttnArgs a) {
     {
         // S(0, 0) and its max
 #pragma unroll
-        for (int st = 0; st < 8; ++st) ak[st] = read_k(kst<0>(), 0, st);
+        for (int st = 0; st < 8; ++st) ak[st] = read_k(0, st);
         const f32x16 zero = {};
 #pragma unroll
         for (int st = 0; st < 8; ++st)
@@ -459,8 +468,8 @@ void k_attn_bf16(AttnArgs a) {
         mta = xhalf_max(x);
         rescale(mta, true);
         if (ragged && t_begin == n_tiles - 1) mask_tail(sa, t_begin * kBN);
-        ak[0] = read_k(kst<0>(), 1, 0);
-        ak[1] = read_k(kst<0>(), 1, 1);
+        ak[0] = read_k(kSubBytes, 0);
+        ak[1] = read_k(kSubBytes, 1);
     }
 
     // Tile t in stage S; on entry sa = S(t, 0) with the reference max already
@@ -473,7 +482,8 @@ void k_attn_bf16(AttnArgs a) {
         constexpr int S = decltype(stage_tag)::value;
         constexpr int S1 = (S + 1) % kStages, S3 = (S + 3) % kStages;
         const bool last = t == t_end - 1;
-        qk_softmax(kst<S>(), 1, sb, sa, pa, ak, vst<S>(), 0, av);
+        constexpr int KS = S * kStageBytes, KS1 = S1 * kStageBytes;
+        qk_softmax(KS + kSubBytes, sb, sa, pa, ak, KS, av);
         // tile t+1 must be in LDS for every wave (tile t+2 may still be in
         // flight), and every wave is past its reads of tile t-1, whose stage
         // is refilled
@@ -483,11 +493,11 @@ void k_attn_bf16(AttnArgs a) {
             wait_vm0();
         __syncthreads();
         if (t + 3 < t_end) issue_tile(t + 3, StageTag<S3>{});
-        pv_max(vst<S>(), 0, pa, av, sb, mtb, kst<S1>(), 0, ak);
+        pv_max(KS, pa, av, sb, mtb, KS1, ak);
         rescale(mtb, true);
         if (ragged && t == n_tiles - 1) mask_tail(sb, t * kBN + 32);
-        qk_softmax(kst<S1>(), 0, sa, sb, pbk, ak, vst<S>(), 1, av);
-        pv_max(vst<S>(), 1, pbk, av, sa, mta, kst<S1>(), 1, ak);
+        qk_softmax(KS1, sa, sb, pbk, ak, KS + kSubBytes, av);
+        pv_max(KS + kSubBytes, pbk, av, sa, mta, KS1 + kSubBytes, ak);
         rescale(mta, !last);
         if (ragged && t + 1 == n_tiles - 1 && !last) mask_tail(sa, (t + 1) * kBN);
         return last;

@@ -82,6 +82,31 @@ def test_attention_split_over_cus(odt):
     assert np.abs(lse.cpu().double().numpy()[:, rows] - ref_lse).max() <= 1e-2
 
 
+@pytest.mark.parametrize("wl", [BF, W.WORKLOADS["tiny_f32"]], ids=["bf16", "f32"])
+def test_attention_scores_growing_along_the_keys(wl):
+    """Scores that climb steadily along the keys (each key adds a multiple of
+    one direction that every query shares): the running maximum grows many
+    times over, so the output is rescaled repeatedly.  Against the oracle."""
+    n_q, n_ctx, n_own = 70, 700, 90
+    rng = np.random.default_rng([wl.wid, 7])
+    u = np.ones(wl.head_dim, np.float32) / np.sqrt(wl.head_dim)
+    def rows(n, ramp):
+        x = 0.25 * rng.standard_normal((n, wl.n_heads, wl.head_dim), dtype=np.float32)
+        if ramp is not None:
+            x += (ramp[:, None, None] * u[None, None, :]).astype(np.float32)
+        return W.encode(wl, x)
+    keys = np.arange(n_ctx + n_own, dtype=np.float32)
+    q = rows(n_q, np.full(n_q, 4.0, np.float32))
+    kc, ko = rows(n_ctx, 0.06 * keys[:n_ctx]), rows(n_own, 0.06 * keys[n_ctx:])
+    vc, vo = rows(n_ctx, None), rows(n_own, None)
+    say("attention growing scores", wl.name)
+    out, lse = attend(wl, q, kc, vc, ko, vo, odt=wa.WA_F32, lse=True)
+    ref, ref_lse = oracle.attention(q, kc, vc, ko, vo, wl.softmax_scale)
+    tol = 1e-5 if wl.dtype == W.F32 else 1e-2
+    assert np.abs(to_f64(out) - ref).max() <= tol
+    assert np.abs(lse.cpu().double().numpy() - ref_lse).max() <= tol
+
+
 def test_attention_unit_values_and_reruns_are_bitwise_equal():
     wl = BF
     q, kc, ko = rand_rows(wl, 200, 1), rand_rows(wl, 300, 2), rand_rows(wl, 70, 4)

@@ -198,3 +198,101 @@ def test_full_history_steps():
         if step == 0:
             hist, _ = oracle.attention(q, hist_k, hist_v, ko, vo, wl.softmax_scale, rows=rows)
             assert np.abs(hist - got).max() < 1e-12
+
+
+def test_long_horizon_chunks():
+    """128 resident pages (9.8 GB of bf16 K/V), then 8 chunks in sequence: the
+    page stage over every page in the pool, gather, 4 denoising steps with
+    fresh queries and own K/V, then one new page appended.  Full-size shapes;
+    attention on sampled rows.  No host copy of the pool is kept: the oracle's
+    page means are taken as pages are drawn, and the selected pages are drawn
+    again from their seeds for the gather and attention checks."""
+    wl = W.WORKLOADS["long_horizon"]
+    run = PoolRun(wl, keep_host_pages=False)
+    host_means = np.full((wl.max_pages, wl.n_heads, wl.head_dim), np.nan)
+
+    def append(page):
+        k, _ = run.append(page)
+        host_means[page] = oracle.page_mean(k)
+
+    for j in range(wl.n_pages):
+        append(j)
+    rows = rows_sample(wl.n_q, 6)
+    tol = attention_tolerance(wl)
+    for c in range(wl.chunks):
+        n_live = wl.n_pages + c * wl.appended_per_chunk
+        got_means = run.means[:n_live].cpu().numpy()
+        merr = np.abs(got_means - host_means[:n_live]).max()
+        assert merr <= 1e-12 * max(1.0, np.abs(host_means[:n_live]).max())
+        q0, _, _ = W.chunk_qkv(wl, c, 0)
+        scores = torch.empty(n_live, dtype=torch.float64, device="cuda")
+        say("long horizon chunk", c, "select over", n_live, "pages")
+        idx = wa.wa_select_pages(run.L, to_device(q0), run.means, wl.k_p, n_cand=n_live,
+                                 out_scores=scores)
+        ref = oracle.select_pages(q0, host_means[:n_live], wl.k_p)
+        assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+        assert oracle.boundary_margin(ref["alpha"], wl.k_p) > 1e-9 * np.abs(ref["alpha"]).max()
+        say("long horizon chunk", c, "gather", ref["idx"].tolist())
+        k_ctx, v_ctx = wa.wa_gather(run.L, run.k_pool, run.v_pool, idx, wl.k_p)
+        drawn = [W.page_kv(wl, int(j)) for j in ref["idx"]]
+        hk = np.concatenate([d[0] for d in drawn])
+        hv = np.concatenate([d[1] for d in drawn])
+        del drawn
+        assert to_bits(k_ctx).tobytes() == hk.tobytes()
+        assert to_bits(v_ctx).tobytes() == hv.tobytes()
+        for step in range(wl.steps):
+            q, ko, vo = W.chunk_qkv(wl, c, step)
+            say("long horizon chunk", c, "step", step, "attention")
+            out = wa.wa_block_attention(run.L, to_device(q), k_ctx, v_ctx, to_device(ko),
+                                        to_device(vo), wl.softmax_scale, out_dtype=wa.WA_BF16)
+            ref_out, _ = oracle.attention(q, hk, hv, ko, vo, wl.softmax_scale, rows=rows)
+            err = np.abs(to_f64(out)[rows] - ref_out).max()
+            assert err <= tol, "chunk %d step %d: attention max |err| %g" % (c, step, err)
+        del k_ctx, v_ctx, hk, hv
+        append(wl.n_pages + c)
+    got_means = run.means.cpu().numpy()
+    assert np.abs(got_means - host_means).max() <= 1e-12 * max(1.0, np.abs(host_means).max())
+
+
+def test_prompt_page_full_size():
+    """Prompt stage at full size: 64 pages of 12,480 tokens in 16 chunks of 4,
+    4,096-dim prompts, the top 4 chunks' 16 pages scored, K_p 4, then gather
+    and attention on sampled rows.  The selected pages are drawn again from
+    their seeds for the oracle."""
+    wl = W.WORKLOADS["prompt_page"]
+    run = PoolRun(wl, keep_host_pages=False)
+    host_means = np.full((wl.max_pages, wl.n_heads, wl.head_dim), np.nan)
+    for j in range(wl.n_pages):
+        k, _ = run.append(j)
+        host_means[j] = oracle.page_mean(k)
+    cp, cur = W.chunk_prompts(wl), W.current_prompt(wl)
+    pages = W.chunk_page_map(wl)
+    n_cand = wl.n_cand_groups * wl.pages_per_group
+    out_chunks = torch.empty(wl.n_cand_groups, dtype=torch.int32, device="cuda")
+    out_cand = torch.empty(n_cand, dtype=torch.int32, device="cuda")
+    prompt_dev = dict(chunk_prompts=torch.from_numpy(cp).cuda(),
+                      cur_prompt=torch.from_numpy(cur).cuda(),
+                      chunk_pages=torch.from_numpy(pages).cuda(), n_keep=wl.n_cand_groups,
+                      out_chunks=out_chunks, out_cand=out_cand)
+    q, ko, vo = W.chunk_qkv(wl, 0, 0)
+    scores = torch.empty(n_cand, dtype=torch.float64, device="cuda")
+    say("prompt stage full size: select")
+    idx = wa.wa_select_pages(run.L, to_device(q), run.means, wl.k_p, prompt=prompt_dev,
+                             out_scores=scores)
+    ref = oracle.select_pages(q, host_means, wl.k_p,
+                              prompt=dict(chunk_prompts=cp, cur_prompt=cur, chunk_pages=pages,
+                                          n_keep=wl.n_cand_groups))
+    assert out_chunks.cpu().numpy().tolist() == ref["chunks"].tolist()
+    assert out_cand.cpu().numpy().tolist() == ref["cand"].tolist()
+    assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+    serr = np.abs(scores.cpu().numpy() - ref["alpha"]).max()
+    assert serr <= 1e-12 * max(1.0, np.abs(ref["alpha"]).max())
+    say("prompt stage full size: gather", ref["idx"].tolist())
+    k_ctx, v_ctx = wa.wa_gather(run.L, run.k_pool, run.v_pool, idx, wl.k_p)
+    drawn = [W.page_kv(wl, int(j)) for j in ref["idx"]]
+    hk = np.concatenate([d[0] for d in drawn])
+    hv = np.concatenate([d[1] for d in drawn])
+    assert to_bits(k_ctx).tobytes() == hk.tobytes()
+    assert to_bits(v_ctx).tobytes() == hv.tobytes()
+    rows = rows_sample(wl.n_q, 8)
+    check_attention(wl, q, hk, hv, ko, vo, k_ctx, v_ctx, rows=rows, out_dtypes=[wa.WA_BF16])
