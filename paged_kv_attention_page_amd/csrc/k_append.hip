@@ -29,7 +29,7 @@ ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lan
 }
 
 static ColSumPlan append_plan(int32_t dtype, int64_t hd, int64_t page_tokens) {
-    return colsum_plan(dtype, hd, page_tokens, 16);
+    return colsum_plan(dtype, hd, page_tokens, 8);
 }
 
 size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens) {

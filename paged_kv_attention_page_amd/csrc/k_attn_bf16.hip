@@ -28,12 +28,14 @@
 //    matches P.
 //  * Software pipeline per wave: the Q K^T products of the next sub-tile are
 //    interleaved with the exponentials of the current one, and the P V
-//    products with the next sub-tile's max, so matrix-core and vector work
-//    overlap (the instruction order inside a region is left to the compiler:
-//    with two wavefronts per SIMD, the other wavefront fills the gaps); all
-//    operands and accumulators live in VGPRs.  The output is only rescaled when a
-//    query's max grows by more than 2^8 in the exp2 domain (exact either way:
-//    the final division uses the same reference max).
+//    products with the operand reads of the next region, so matrix-core and
+//    vector work overlap (the instruction order inside a region is left to the
+//    compiler: with two wavefronts per SIMD, the other wavefront fills the
+//    gaps); all operands and accumulators live in VGPRs.
+//  * Lazy rescaling without a running maximum: probabilities are taken against
+//    a reference max that moves only when a row's probabilities of one
+//    sub-tile sum past 2^8; then O and l are rescaled and that sub-tile is
+//    recomputed (exact either way: the final division uses the same reference).
 #include <math.h>
 
 #include "wa_internal.h"
@@ -56,7 +58,12 @@ static constexpr int kStages = 4;         // LDS ring depth (tiles)
 static constexpr int kTileElems = kBN * kD;
 static constexpr int kRowsPerWave = kBN / kWaves;   // tile rows each wavefront copies
 static constexpr int kCopies = kRowsPerWave / 4;    // 1 KB copies per tensor per wavefront
-static constexpr float kRescaleLog2 = 8.f;   // rescale when the max grows by > 2^8
+// The probabilities of a sub-tile are taken against a reference max m that
+// only moves when a row's new probabilities sum past 2^8 (some score more than
+// 2^4 above m, or an overflow): O and l are then rescaled and the sub-tile's
+// probabilities recomputed.  The result is exact either way, since O and l
+// always share the reference max, and no per-sub-tile maximum is needed.
+static constexpr float kSumLimit = 256.f;
 static constexpr int kMaxSplitBlocks = 256;  // blocks of a split launch (partial slots)
 static constexpr int kMinSplitTiles = 16;    // fewest tiles per block worth a split
 static constexpr int kMaxBlocksPerItem = 32; // split blocks per (query block, head) item
@@ -217,7 +224,6 @@ void k_attn_bf16(AttnArgs a) {
     const int n_tiles = a.n_tiles;
     const bool ragged = (n_keys % kBN) != 0;
     const float c = a.c;
-    const float thr = kRescaleLog2 / c;   // raw-score growth that forces a rescale
 
     // ---- tile loads: wavefront w copies rows 8w ... 8w+7 of the K and V
     // tiles, 4 rows (1 KB) per instruction; lane -> (row 8w+4i+lane/16, slot lane%16)
@@ -357,7 +363,7 @@ void k_attn_bf16(AttnArgs a) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
-    float m = -INFINITY, l = 0.f;
+    float m = -3.0e38f, l = 0.f;   // finite: no inf - inf anywhere
 
     // ---- keys past the end (last tile only) get score -inf.  Their rows were
     // loaded as copies of the last key, so maxima taken before masking are
@@ -372,33 +378,16 @@ void k_attn_bf16(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
             if (8 * (i >> 2) + (i & 3) >= lim) s[i] = -INFINITY;
     };
-    // ---- move the reference max (and rescale the output) when it grew enough
-    auto rescale = [&](float mt, bool live) __attribute__((always_inline)) {
-        const bool grow = live && mt > m + thr;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            // a real branch: without this marker the compiler flattens it and
-            // rescales the whole output on every sub-tile
-            asm volatile("; rescale" ::: "memory");
-            const float mn = fmaxf(m, mt);
-            const float corr = __builtin_amdgcn_exp2f((m - mn) * c);
-            l *= corr;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[b][i] *= corr;
-            m = mn;
-        }
-    };
-
-    // ---- fused region QK+SOFTMAX: sn = K(kt, sub) Q^T (8 MFMAs) interleaved
-    // with the exponentials of sc (2 elements per MFMA), P packed to bf16 for
-    // the P V products, l accumulated from the bf16 values.  ak[0], ak[1]
-    // arrive prefetched; the V^T operands 0 and 1 of the following P V region
-    // (sub-tile vsub of vt) are prefetched at the end.
+    // ---- region QK+SOFTMAX: sn = K Q^T of the sub-tile at koff (8 MFMAs)
+    // interleaved with the exponentials of sc (2 elements per MFMA), P packed to
+    // bf16 for the P V products, l accumulated from the bf16 values; then the
+    // lazy-rescale test (see kSumLimit).  ak[0], ak[1] arrive prefetched; the
+    // V^T operands 0 and 1 of the following P V region (at voff) are prefetched
+    // at the end.
     auto qk_softmax = [&](int koff, f32x16 &sn, const f32x16 &sc, bf16x8 (&pb)[2],
                           bf16x8 (&ak)[8], int voff, bf16x8 (&av)[8]) __attribute__((always_inline)) {
         const float mc = m * c;
-        float ls = l;
+        float ls0 = 0.f, ls1 = 0.f;
         const f32x16 zero = {};
         const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
@@ -409,28 +398,52 @@ void k_attn_bf16(AttnArgs a) {
             const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
             pb[st >> 2][2 * (st & 3)] = pr[0];
             pb[st >> 2][2 * (st & 3) + 1] = pr[1];
-            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls, false);
+            if (st & 1) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls1, false);
+            else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls0, false);
             if (st + 2 < 8) ak[st + 2] = read_k(koff, st + 2);
             if (st >= 6) av[st - 6] = read_v(voff, st - 6);
         }
-        l = ls;
+        float lsub = ls0 + ls1;
+        if (__builtin_amdgcn_ballot_w64(lsub > kSumLimit) != 0) {
+            asm volatile("; rescale" ::: "memory");
+            float x = fmaxf(sc[0], sc[1]);
+#pragma unroll
+            for (int i = 1; i < 8; ++i) x = fmaxf(x, fmaxf(sc[2 * i], sc[2 * i + 1]));
+            const float mn = fmaxf(m, xhalf_max(x));
+            const float corr = __builtin_amdgcn_exp2f((m - mn) * c);
+            l *= corr;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[b][i] *= corr;
+            m = mn;
+            const float mc2 = m * c;
+            lsub = 0.f;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st], c, -mc2));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st + 1], c, -mc2));
+                const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
+                pb[st >> 2][2 * (st & 3)] = pr[0];
+                pb[st >> 2][2 * (st & 3) + 1] = pr[1];
+                lsub = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsub, false);
+            }
+        }
+        l += lsub;
     };
 
-    // ---- fused region PV+MAX: O^T += V^T P^T (8 MFMAs) interleaved with the
-    // max of sn per query; prefetches the next V^T operands two steps ahead and,
-    // at the end, the first two K operands of the next QK+SOFTMAX region.
-    auto pv_max = [&](int voff, const bf16x8 (&pb)[2], bf16x8 (&av)[8], const f32x16 &sn,
-                      float &mt, int koff_next, bf16x8 (&ak)[8]) __attribute__((always_inline)) {
-        float x = fmaxf(sn[0], sn[1]);
+    // ---- region PV: O^T += V^T P^T (8 MFMAs); prefetches the next V^T
+    // operands two steps ahead and, at the end, the first two K operands of the
+    // next QK+SOFTMAX region.
+    auto pv = [&](int voff, const bf16x8 (&pb)[2], bf16x8 (&av)[8], int koff_next,
+                  bf16x8 (&ak)[8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int op = 0; op < 8; ++op) {
             const int jj = op >> 2, b = op & 3;
             o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[op], pb[jj], o[b], 0, 0, 0);
-            if (op < 7) x = fmaxf(x, fmaxf(sn[2 + 2 * op], sn[3 + 2 * op]));
             if (op + 2 < 8) av[op + 2] = read_v(voff, op + 2);
             if (op >= 6) ak[op - 6] = read_k(koff_next, op - 6);
         }
-        mt = xhalf_max(x);
     };
 
     // ---- prologue: every wave is past its reads of the previous segment's
@@ -453,20 +466,14 @@ void k_attn_bf16(AttnArgs a) {
     f32x16 sa, sb;
     bf16x8 pa[2], pbk[2];
     bf16x8 ak[8], av[8];
-    float mta, mtb;
     {
-        // S(0, 0) and its max
+        // S of the segment's first sub-tile
 #pragma unroll
         for (int st = 0; st < 8; ++st) ak[st] = read_k(0, st);
         const f32x16 zero = {};
 #pragma unroll
         for (int st = 0; st < 8; ++st)
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sa, 0, 0, 0);
-        float x = sa[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[i]);
-        mta = xhalf_max(x);
-        rescale(mta, true);
         if (ragged && t_begin == n_tiles - 1) mask_tail(sa, t_begin * kBN);
         ak[0] = read_k(kSubBytes, 0);
         ak[1] = read_k(kSubBytes, 1);
@@ -493,12 +500,10 @@ void k_attn_bf16(AttnArgs a) {
             wait_vm0();
         __syncthreads();
         if (t + 3 < t_end) issue_tile(t + 3, StageTag<S3>{});
-        pv_max(KS, pa, av, sb, mtb, KS1, ak);
-        rescale(mtb, true);
+        pv(KS, pa, av, KS1, ak);
         if (ragged && t == n_tiles - 1) mask_tail(sb, t * kBN + 32);
         qk_softmax(KS1, sa, sb, pbk, ak, KS + kSubBytes, av);
-        pv_max(KS + kSubBytes, pbk, av, sa, mta, KS1 + kSubBytes, ak);
-        rescale(mta, !last);
+        pv(KS + kSubBytes, pbk, av, KS1 + kSubBytes, ak);
         if (ragged && t + 1 == n_tiles - 1 && !last) mask_tail(sa, (t + 1) * kBN);
         return last;
     };
