@@ -170,7 +170,6 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
     const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
     return (T *)(uintptr_t)(lo | (hi << 32));
 }
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 
@@ -447,20 +446,21 @@ void k_attn_bf16(AttnArgs a) {
     };
 
     // ---- prologue: every wave is past its reads of the previous segment's
-    // tiles; tiles t_begin .. t_begin+2 in flight, wait for t_begin
+    // tiles; tiles t_begin .. t_begin+2 in flight, wait for t_begin.  Every
+    // issue names a tile: near the end of the segment, the last tile again
+    // (into a stage nobody reads), so that each tile issues the same number
+    // of copies and one fixed vmcnt wait fits every tile.
     static_assert(2 * kCopies == 4, "the waits below count 4 copies per tile");
     __syncthreads();
+    const int t_last = t_end - 1;
+    // the tile whose second half is masked, and the one before it (whose
+    // successor's first half is masked); -2 when the keys fill every tile
+    const int mask_tile = ragged ? n_tiles - 1 : -2;
+    const int mask_tile_prev = ragged ? n_tiles - 2 : -2;
     issue_tile(t_begin, StageTag<0>{});
-    if (t_end - t_begin > 2) {
-        issue_tile(t_begin + 1, StageTag<1>{});
-        issue_tile(t_begin + 2, StageTag<2>{});
-        wait_vm8();
-    } else if (t_end - t_begin > 1) {
-        issue_tile(t_begin + 1, StageTag<1>{});
-        wait_vm4();
-    } else {
-        wait_vm0();
-    }
+    issue_tile(min(t_begin + 1, t_last), StageTag<1>{});
+    issue_tile(min(t_begin + 2, t_last), StageTag<2>{});
+    wait_vm8();
     __syncthreads();
 
     f32x16 sa, sb;
@@ -482,29 +482,27 @@ void k_attn_bf16(AttnArgs a) {
     // Tile t in stage S; on entry sa = S(t, 0) with the reference max already
     // moved, and the first two K operands of S(t, 1) prefetched.  Stages S+1
     // and S+2 hold (or are receiving) tiles t+1 and t+2; stage S+3 is refilled
-    // with tile t+3.  On exit sa = S(t+1, 0), likewise.  The last tile runs the same code: its products of
-    // the (nonexistent) next tile read a stale stage and are discarded, which
-    // keeps every fused region one basic block.
+    // with tile min(t+3, last).  On exit sa = S(t+1, 0), likewise.  The last
+    // tile runs the same code: its products of the (nonexistent) next tile
+    // read a stale stage and are discarded, which keeps every fused region one
+    // basic block.
     auto tile = [&](int t, auto stage_tag) __attribute__((always_inline)) -> bool {
         constexpr int S = decltype(stage_tag)::value;
         constexpr int S1 = (S + 1) % kStages, S3 = (S + 3) % kStages;
         const bool last = t == t_end - 1;
         constexpr int KS = S * kStageBytes, KS1 = S1 * kStageBytes;
         qk_softmax(KS + kSubBytes, sb, sa, pa, ak, KS, av);
-        // tile t+1 must be in LDS for every wave (tile t+2 may still be in
-        // flight), and every wave is past its reads of tile t-1, whose stage
-        // is refilled
-        if (t + 2 < t_end)
-            wait_vm4();
-        else
-            wait_vm0();
+        // tile t+1 must be in LDS for every wave (the copies of tile t+2 may
+        // still be in flight: exactly 4 of them), and every wave is past its
+        // reads of tile t-1, whose stage is refilled
+        wait_vm4();
         __syncthreads();
-        if (t + 3 < t_end) issue_tile(t + 3, StageTag<S3>{});
+        issue_tile(min(t + 3, t_last), StageTag<S3>{});
         pv(KS, pa, av, KS1, ak);
-        if (ragged && t == n_tiles - 1) mask_tail(sb, t * kBN + 32);
+        if (t == mask_tile) mask_tail(sb, t * kBN + 32);
         qk_softmax(KS1, sa, sb, pbk, ak, KS + kSubBytes, av);
         pv(KS + kSubBytes, pbk, av, KS1 + kSubBytes, ak);
-        if (ragged && t + 1 == n_tiles - 1 && !last) mask_tail(sa, (t + 1) * kBN);
+        if (t == mask_tile_prev && !last) mask_tail(sa, (t + 1) * kBN);
         return last;
     };
     for (int t = t_begin;; t += 4) {
