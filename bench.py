@@ -169,6 +169,34 @@ def main():
     split = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sev]))
              for i, n in enumerate(("select", "gather"))}
 
+    # paged pass (after the timed region; not part of the step figure): the
+    # same step with the attention reading the selected pages in place from
+    # the pool (wa_paged_attention) instead of gather + attention over the copy
+    def step_paged(ev=None):
+        wa.wa_append_page(L, k_new, v_new, k_pool, v_pool, spare, means, workspace=ws_append,
+                          stream=stream)
+        wa.wa_select_pages(L, q, means, wl.k_p, cand=cand, out_idx=idx, workspace=ws_sel,
+                           stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        wa.wa_paged_attention(L, q, k_pool, v_pool, idx, wl.k_p, k_own, v_own, wl.softmax_scale,
+                              out_dtype=wa.WA_BF16, out=out, workspace=ws_attn, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    n_paged = args.steps
+    for _ in range(5):
+        step_paged()
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_paged)]
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for k in range(n_paged):
+        step_paged(pev[k])
+    torch.cuda.synchronize()
+    tp1 = time.perf_counter()
+    paged_ms_step = (tp1 - tp0) * 1e3 / n_paged
+    paged_attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+
     attn_tflops = flops / (avg["attention"] * 1e-3) / 1e12
     sg_gbps = (bytes_select + bytes_gather) / (avg["select_gather"] * 1e-3) / 1e9
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -217,6 +245,14 @@ def main():
         "append": {
             "bytes": bytes_append,
             "GB/s": round(bytes_append / (avg["append"] * 1e-3) / 1e9, 1),
+        },
+        "paged": {
+            "note": "append + select + wa_paged_attention (pages read in place, no gather), "
+                    "same inputs, timed after the step figure",
+            "ms_per_step": round(paged_ms_step, 4),
+            "attention_ms": round(paged_attn_ms, 4),
+            "attention_TFLOP/s": round(flops / (paged_attn_ms * 1e-3) / 1e12, 2),
+            "step_speedup_vs_gathered": round(ms_per_step / paged_ms_step, 4),
         },
         "flops_per_step": flops,
         "cpu_baseline": None,

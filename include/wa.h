@@ -12,7 +12,9 @@
  *                      prompt stage that picks the candidate chunks);
  *   wa_gather          copy the kept pages into one contiguous K/V buffer;
  *   wa_block_attention unmasked softmax attention of the chunk's queries over
- *                      the gathered pages followed by the chunk's own K/V.
+ *                      the gathered pages followed by the chunk's own K/V;
+ *   wa_paged_attention the same attention reading the kept pages in place
+ *                      from the pool (no gathered copy).
  *
  * Sources (page title, section):
  *   WorldAttention review, "WorldAttention: An Efficient Attention
@@ -221,6 +223,33 @@ wa_status wa_block_attention(const wa_layout *layout, const void *q, int32_t n_q
  * arguments and the device's compute-unit count; launches nothing. */
 size_t wa_attention_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ctx,
                                     int32_t n_own);
+
+/*
+ * Paged block attention: the same result as wa_gather into k_ctx / v_ctx
+ * followed by wa_block_attention over them, without the copy.  The context
+ * keys are read in place from the pool pages idx[0 .. k_p-1] (key n is token
+ * n % page_tokens of page idx[n / page_tokens], n < k_p * page_tokens), then
+ * the n_own keys of k_own / v_own; one softmax, no mask.  The WorldAttention
+ * review (its Tab. 9, in "Strengths") finds that rebuilding and copying the
+ * retrieved KV into a contiguous buffer is the largest share of the sparse
+ * path's time; reading the pages where they lie removes that copy, for every
+ * denoising step.
+ *
+ * k_pool, v_pool: [max_pages][page_tokens][H][d] (16-byte aligned).
+ * idx: device [k_p] int32 pool slots, read on the device; every entry must be
+ * in [0, max_pages) (an entry outside is clamped into the pool so that no
+ * access leaves it, and the result is then unspecified).  Other arguments,
+ * precision, workspace (wa_attention_workspace_bytes with n_ctx =
+ * k_p * page_tokens) and errors as wa_block_attention, plus: NULL k_pool /
+ * v_pool / idx, k_p < 1, page_tokens or max_pages < 1 -> WA_ERR_INVALID_ARG.
+ * The fast path reads whole 64-key tiles from one page and needs
+ * page_tokens % 64 == 0 (bf16); other page sizes take a slower per-row path.
+ */
+wa_status wa_paged_attention(const wa_layout *layout, const void *q, int32_t n_q,
+                             const void *k_pool, const void *v_pool, const int32_t *idx,
+                             int32_t k_p, const void *k_own, const void *v_own, int32_t n_own,
+                             float softmax_scale, int32_t out_dtype, void *out, float *lse,
+                             void *workspace, size_t ws_bytes, void *stream);
 
 /* Static text describing a status code. */
 const char *wa_status_string(wa_status status);

@@ -24,7 +24,7 @@ __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "W
            "Layout", "PromptStage", "WaError", "load_library", "library_path", "layout",
            "wa_append_workspace_bytes", "wa_append_page", "wa_select_workspace_bytes",
            "wa_select_pages", "wa_gather", "wa_attention_workspace_bytes", "wa_block_attention",
-           "wa_status_string"]
+           "wa_paged_attention", "wa_status_string"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -100,6 +100,9 @@ def load_library():
     lib.wa_attention_workspace_bytes.restype = sz
     lib.wa_block_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, i32, p, p, p, sz, p]
     lib.wa_block_attention.restype = i32
+    lib.wa_paged_attention.argtypes = [L, p, i32, p, p, p, i32, p, p, i32, f32, i32, p, p, p, sz,
+                                       p]
+    lib.wa_paged_attention.restype = i32
     lib.wa_status_string.argtypes = [i32]
     lib.wa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -310,4 +313,45 @@ def wa_block_attention(L: Layout, q, k_ctx, v_ctx, k_own, v_own, softmax_scale=N
                                 float(softmax_scale), int(out_dtype), _ptr(out), _ptr(lse),
                                 _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "wa_block_attention")
+    return out
+
+
+def wa_paged_attention(L: Layout, q, k_pool, v_pool, idx, k_p, k_own, v_own, softmax_scale=None,
+                       out_dtype=None, out=None, lse=None, workspace=None, stream=None):
+    """Attention of q over [pages idx[0..k_p) of the pools ++ k_own], read in
+    place; the same result as wa_gather followed by wa_block_attention."""
+    lib = load_library()
+    dt = L.torch_dtype
+    row = L.row_elems
+    _need(q, "q", dt)
+    n_q = q.numel() // row
+    pool_elems = L.max_pages * L.page_tokens * row
+    _need(k_pool, "k_pool", dt, pool_elems)
+    _need(v_pool, "v_pool", dt, pool_elems)
+    _need(idx, "idx", torch.int32, int(k_p))
+    n_own = 0
+    if k_own is not None or v_own is not None:
+        _need(k_own, "k_own", dt)
+        _need(v_own, "v_own", dt)
+        n_own = k_own.numel() // row
+        if k_own.numel() % row or v_own.numel() != k_own.numel():
+            raise ValueError("k_own / v_own are not matching whole token rows")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (L.head_dim ** 0.5)
+    if out_dtype is None:
+        out_dtype = L.dtype
+    odt = _TORCH_DTYPE[out_dtype]
+    if out is None:
+        out = torch.empty((n_q, L.n_heads, L.head_dim), dtype=odt, device=q.device)
+    _need(out, "out", odt, n_q * row)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, n_q * L.n_heads)
+    n_ctx = int(k_p) * L.page_tokens
+    nbytes = lib.wa_attention_workspace_bytes(ctypes.byref(L), int(n_q), int(n_ctx), int(n_own))
+    ws = _workspace(nbytes, workspace, q)
+    st = lib.wa_paged_attention(ctypes.byref(L), _ptr(q), int(n_q), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(idx), int(k_p), _ptr(k_own), _ptr(v_own), int(n_own),
+                                float(softmax_scale), int(out_dtype), _ptr(out), _ptr(lse),
+                                _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "wa_paged_attention")
     return out

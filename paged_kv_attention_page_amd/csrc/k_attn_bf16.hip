@@ -95,6 +95,13 @@ struct AttnArgs {
     float *lse;
     float *part_o;      // [items][slots][kBM][kD] unnormalised partial outputs
     float *part_ml;     // [items][slots][kBM][2] reference max and row sum
+    // paged context (idx != null): k_ctx / v_ctx are the pools, context key n
+    // is token n % page_tokens of pool page idx[n / page_tokens]
+    const int32_t *idx;
+    int page_tokens;
+    int max_pages;
+    int tpp;            // 64-key tiles per page when page_tokens % 64 == 0, else 0
+    uint64_t page_bytes;   // pool page stride in bytes
 };
 
 // Work order of a split launch.  Position g in [0, items * T) names one 64-key
@@ -210,6 +217,12 @@ __device__ __forceinline__ uint16_t *vst() {
     return lds_ring + (kStages + S) * kTileElems;
 }
 
+// Where the context keys come from (see AttnArgs): MODE 0, one contiguous
+// buffer; MODE 1, pool pages through a.idx, page_tokens a multiple of 64
+// (whole tiles per page: the copies take the same fast path as a contiguous
+// buffer); MODE 2, pool pages, other page sizes (context tiles copied row by
+// row).
+template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bf16(AttnArgs a) {
 
@@ -308,17 +321,39 @@ void k_attn_bf16(AttnArgs a) {
         koff[i] = rowb + 16u * (unsigned)(ld_slot ^ (row & 15));
         voff[i] = rowb + 16u * (unsigned)(ld_slot ^ (4 * (row & 3)));
     }
+    // paged context with whole tiles per page (page_tokens % 64 == 0): the
+    // page of the context tile the copies reach next.  Its base is shifted
+    // back by the tiles of the pages before it, so that tile t's first row
+    // is at base + t * tile_bytes as in a contiguous buffer.  Tiles are
+    // issued in increasing order, so the page only moves forward, one page at
+    // a time, with one scalar load of its id.  An id outside the pool is
+    // clamped into it (memory safety only: the caller passes valid ids).
+    int pg = 0, pg_next = 0x7fffffff;   // pg_next: first tile of the next page
+    uint64_t kb_pg = kb_ctx, vb_pg = vb_ctx;
+    auto set_page = [&](int r) __attribute__((always_inline)) {
+        asm volatile("; set page" ::: "memory");
+        int id = __builtin_amdgcn_readfirstlane(a.idx[r]);
+        id = id < 0 ? 0 : (id >= a.max_pages ? a.max_pages - 1 : id);
+        pg = r;
+        pg_next = (r + 1) * a.tpp < t_ctx ? (r + 1) * a.tpp : 0x7fffffff;
+        const uint64_t back = (uint64_t)(uint32_t)(r * a.tpp) * tile_bytes;
+        kb_pg = kb_ctx + (uint64_t)(uint32_t)id * a.page_bytes - back;
+        vb_pg = vb_ctx + (uint64_t)(uint32_t)id * a.page_bytes - back;
+    };
+    if (MODE == 1 && t_begin < t_ctx) set_page(t_begin / a.tpp);
+
     static_assert(kCopies == 2, "issue_tile writes two 1 KB copies per tensor");
     auto issue_tile = [&](int t, auto stage_tag) __attribute__((always_inline)) {
         constexpr unsigned S = decltype(stage_tag)::value;
         constexpr unsigned OK = S * kTileBytes, OV = (kStages + S) * kTileBytes;
         constexpr unsigned ROWS4 = 4 * kD * 2;    // four tile rows
         const int key0 = t * kBN;
-        if (t != t_mid && t < t_full) {
+        if (t != t_mid && t < t_full && (MODE != 2 || t >= t_ctx)) {
             const uint64_t off = (uint64_t)(uint32_t)t * tile_bytes;
             const bool in_ctx = t < t_ctx;
-            const uint16_t *kb = uniform_ptr((const uint16_t *)(uintptr_t)((in_ctx ? kb_ctx : kb_own) + off));
-            const uint16_t *vb = uniform_ptr((const uint16_t *)(uintptr_t)((in_ctx ? vb_ctx : vb_own) + off));
+            if (MODE == 1 && t >= pg_next) set_page(pg + 1);
+            const uint16_t *kb = uniform_ptr((const uint16_t *)(uintptr_t)((in_ctx ? kb_pg : kb_own) + off));
+            const uint16_t *vb = uniform_ptr((const uint16_t *)(uintptr_t)((in_ctx ? vb_pg : vb_own) + off));
             dma16_sbase<OK>(kb, koff[0], ld_base);
             dma16_sbase<OV>(vb, voff[0], ld_base);
             dma16_sbase<OK + ROWS4>(kb, koff[1], ld_base);
@@ -334,10 +369,18 @@ void k_attn_bf16(AttnArgs a) {
             int n = key0 + row;
             n = n < n_keys ? n : n_keys - 1;           // rows past the end repeat the last key
             const bool in_ctx = n < a.n_ctx;
-            const int64_t off = (int64_t)(in_ctx ? n : n - a.n_ctx) * hd + h * kD;
+            int64_t row_at = in_ctx ? n : n - a.n_ctx;   // row in its buffer
+            if (MODE == 2 && in_ctx) {
+                const int r = n / a.page_tokens;
+                int id = a.idx[r];
+                id = id < 0 ? 0 : (id >= a.max_pages ? a.max_pages - 1 : id);
+                row_at = (int64_t)id * a.page_tokens + (n - r * a.page_tokens);
+            }
+            const int64_t off = row_at * hd + h * kD;
             kr[i] = (in_ctx ? k_ctx : k_own) + off + 8 * (ld_slot ^ (row & 15));
             vr[i] = (in_ctx ? v_ctx : v_own) + off + 8 * (ld_slot ^ (4 * (row & 3)));
         }
+        asm volatile("; dma slow path copies" ::: "memory");
         dma16<OK>(kr[0], ld_base);
         dma16<OV>(vr[0], ld_base);
         dma16<OK + ROWS4>(kr[1], ld_base);
@@ -678,7 +721,8 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
                                  const uint16_t *k_ctx, const uint16_t *v_ctx, int32_t n_ctx,
                                  const uint16_t *k_own, const uint16_t *v_own, int32_t n_own,
                                  float scale, int32_t out_dtype, void *out, float *lse,
-                                 const AttnPlan &plan, void *workspace, hipStream_t s) {
+                                 const AttnPlan &plan, void *workspace, const PagedCtx &pg,
+                                 hipStream_t s) {
     AttnArgs a;
     a.q = q;
     a.k_ctx = k_ctx;
@@ -703,7 +747,17 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
     a.lse = lse;
     a.part_o = plan.split ? (float *)workspace : nullptr;
     a.part_ml = plan.split ? (float *)workspace + (size_t)plan.items * plan.slots * kBM * kD : nullptr;
-    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)plan.grid), dim3(kThreads), 0, s, a);
+    a.idx = pg.idx;
+    a.page_tokens = pg.page_tokens;
+    a.max_pages = pg.max_pages;
+    a.tpp = pg.idx && pg.page_tokens % kBN == 0 ? pg.page_tokens / kBN : 0;
+    a.page_bytes = (uint64_t)pg.page_tokens * (uint64_t)n_heads * kD * 2u;
+    if (!pg.idx)
+        hipLaunchKernelGGL(k_attn_bf16<0>, dim3((unsigned)plan.grid), dim3(kThreads), 0, s, a);
+    else if (a.tpp > 0)
+        hipLaunchKernelGGL(k_attn_bf16<1>, dim3((unsigned)plan.grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_attn_bf16<2>, dim3((unsigned)plan.grid), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !plan.split) return e;
     hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(a.q_blocks * n_heads * (kBM / kMergeRows))),

@@ -1,6 +1,6 @@
 // fp32 block attention (Inferix summary, section 3.4, Step 3): each query of
-// the chunk attends over the gathered pages followed by the chunk's own K/V,
-// one softmax, no mask.  Used for fp32 layouts (head_dim 64 or 128), where
+// the chunk attends over the gathered pages (or, paged, the selected pool
+// pages read in place) followed by the chunk's own K/V, one softmax, no mask.  Used for fp32 layouts (head_dim 64 or 128), where
 // exactness matters more than speed; plain FMA arithmetic, no matrix cores.
 //
 // Block = 64 queries of one head; 4 threads per query, each owning d/4 of
@@ -24,7 +24,9 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *__restrict__ q, i
                                                   const float *__restrict__ k_own,
                                                   const float *__restrict__ v_own, int n_own,
                                                   int n_heads, float c, float *__restrict__ out,
-                                                  float *__restrict__ lse) {
+                                                  float *__restrict__ lse,
+                                                  const int32_t *__restrict__ idx, int page_tokens,
+                                                  int max_pages) {
     constexpr int DQ = D / 4;   // dims per thread
     __shared__ float ks[kF32Keys][D];
     __shared__ float vs[kF32Keys][D];
@@ -51,8 +53,18 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *__restrict__ q, i
             const int n = k0 + row;
             float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
             if (n < n_keys) {
-                const float *kb = n < n_ctx ? k_ctx + (int64_t)n * hd : k_own + (int64_t)(n - n_ctx) * hd;
-                const float *vb = n < n_ctx ? v_ctx + (int64_t)n * hd : v_own + (int64_t)(n - n_ctx) * hd;
+                // context row n: row n of the gathered buffer, or (paged) token
+                // n % page_tokens of pool page idx[n / page_tokens], the id
+                // clamped into the pool (memory safety only)
+                int64_t row = n;
+                if (idx && n < n_ctx) {
+                    const int r = n / page_tokens;
+                    int id = idx[r];
+                    id = id < 0 ? 0 : (id >= max_pages ? max_pages - 1 : id);
+                    row = (int64_t)id * page_tokens + (n - r * page_tokens);
+                }
+                const float *kb = n < n_ctx ? k_ctx + row * hd : k_own + (int64_t)(n - n_ctx) * hd;
+                const float *vb = n < n_ctx ? v_ctx + row * hd : v_own + (int64_t)(n - n_ctx) * hd;
                 kk = *(const float4 *)(kb + h * D + cv * 4);
                 vv = *(const float4 *)(vb + h * D + cv * 4);
             }
@@ -98,15 +110,18 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *__restrict__ q, i
 hipError_t launch_attention_f32(int32_t n_heads, int32_t head_dim, const float *q, int32_t n_q,
                                 const float *k_ctx, const float *v_ctx, int32_t n_ctx,
                                 const float *k_own, const float *v_own, int32_t n_own,
-                                float scale, float *out, float *lse, hipStream_t s) {
+                                float scale, float *out, float *lse, const PagedCtx &pg,
+                                hipStream_t s) {
     const float c = scale * 1.4426950408889634f;
     const dim3 grid((unsigned)((n_q + kF32Queries - 1) / kF32Queries), (unsigned)n_heads);
     if (head_dim == 64)
         hipLaunchKernelGGL(k_attn_f32<64>, grid, dim3(256), 0, s, q, n_q, k_ctx, v_ctx, n_ctx,
-                           k_own, v_own, n_own, n_heads, c, out, lse);
+                           k_own, v_own, n_own, n_heads, c, out, lse, pg.idx, pg.page_tokens,
+                           pg.max_pages);
     else
         hipLaunchKernelGGL(k_attn_f32<128>, grid, dim3(256), 0, s, q, n_q, k_ctx, v_ctx, n_ctx,
-                           k_own, v_own, n_own, n_heads, c, out, lse);
+                           k_own, v_own, n_own, n_heads, c, out, lse, pg.idx, pg.page_tokens,
+                           pg.max_pages);
     return hipGetLastError();
 }
 

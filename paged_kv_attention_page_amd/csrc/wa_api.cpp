@@ -130,13 +130,14 @@ size_t wa_attention_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_c
     return attention_plan(L->n_heads, n_q, n_ctx + n_own, current_cu_count()).workspace;
 }
 
-wa_status wa_block_attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
-                             const void *v_ctx, int32_t n_ctx, const void *k_own,
-                             const void *v_own, int32_t n_own, float softmax_scale,
-                             int32_t out_dtype, void *out, float *lse, void *workspace,
-                             size_t ws_bytes, void *stream) {
-    wa_status st = check_layout(L, false);
-    if (st != WA_OK) return st;
+namespace {
+
+// Shared by wa_block_attention and wa_paged_attention: the layout is already
+// checked, and pg says where the n_ctx context keys come from.
+wa_status attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
+                    const void *v_ctx, int32_t n_ctx, const void *k_own, const void *v_own,
+                    int32_t n_own, float softmax_scale, int32_t out_dtype, void *out, float *lse,
+                    void *workspace, size_t ws_bytes, const PagedCtx &pg, void *stream) {
     if (!q || !out) return WA_ERR_INVALID_ARG;
     if (n_q < 1 || n_ctx < 0 || n_own < 0 || (int64_t)n_ctx + n_own < 1) return WA_ERR_INVALID_ARG;
     if ((int64_t)n_ctx + n_own > 0x7fffffff - 256) return WA_ERR_UNSUPPORTED;
@@ -152,7 +153,8 @@ wa_status wa_block_attention(const wa_layout *L, const void *q, int32_t n_q, con
         return from_hip(launch_attention_f32(L->n_heads, L->head_dim, (const float *)q, n_q,
                                              (const float *)k_ctx, (const float *)v_ctx, n_ctx,
                                              (const float *)k_own, (const float *)v_own, n_own,
-                                             softmax_scale, (float *)out, lse, (hipStream_t)stream));
+                                             softmax_scale, (float *)out, lse, pg,
+                                             (hipStream_t)stream));
     }
     if (L->head_dim != 128) return WA_ERR_UNSUPPORTED;
     if (out_dtype != WA_F32 && out_dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
@@ -162,8 +164,40 @@ wa_status wa_block_attention(const wa_layout *L, const void *q, int32_t n_q, con
     return from_hip(launch_attention_bf16(L->n_heads, (const uint16_t *)q, n_q,
                                           (const uint16_t *)k_ctx, (const uint16_t *)v_ctx, n_ctx,
                                           (const uint16_t *)k_own, (const uint16_t *)v_own, n_own,
-                                          softmax_scale, out_dtype, out, lse, plan, workspace,
+                                          softmax_scale, out_dtype, out, lse, plan, workspace, pg,
                                           (hipStream_t)stream));
+}
+
+}  // namespace
+
+wa_status wa_block_attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
+                             const void *v_ctx, int32_t n_ctx, const void *k_own,
+                             const void *v_own, int32_t n_own, float softmax_scale,
+                             int32_t out_dtype, void *out, float *lse, void *workspace,
+                             size_t ws_bytes, void *stream) {
+    const wa_status st = check_layout(L, false);
+    if (st != WA_OK) return st;
+    return attention(L, q, n_q, k_ctx, v_ctx, n_ctx, k_own, v_own, n_own, softmax_scale,
+                     out_dtype, out, lse, workspace, ws_bytes, PagedCtx{}, stream);
+}
+
+wa_status wa_paged_attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_pool,
+                             const void *v_pool, const int32_t *idx, int32_t k_p,
+                             const void *k_own, const void *v_own, int32_t n_own,
+                             float softmax_scale, int32_t out_dtype, void *out, float *lse,
+                             void *workspace, size_t ws_bytes, void *stream) {
+    const wa_status st = check_layout(L, true);
+    if (st != WA_OK) return st;
+    if (!k_pool || !v_pool || !idx) return WA_ERR_INVALID_ARG;
+    if (k_p < 1) return WA_ERR_INVALID_ARG;
+    if ((int64_t)k_p * L->page_tokens > 0x7fffffff - 256) return WA_ERR_UNSUPPORTED;
+    if ((uintptr_t)idx & 3u) return WA_ERR_INVALID_ARG;
+    PagedCtx pg;
+    pg.idx = idx;
+    pg.page_tokens = L->page_tokens;
+    pg.max_pages = L->max_pages;
+    return attention(L, q, n_q, k_pool, v_pool, k_p * L->page_tokens, k_own, v_own, n_own,
+                     softmax_scale, out_dtype, out, lse, workspace, ws_bytes, pg, stream);
 }
 
 const char *wa_status_string(wa_status s) {

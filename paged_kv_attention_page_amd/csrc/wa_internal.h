@@ -69,10 +69,21 @@ hipError_t launch_gather(const wa_layout &L, const void *k_pool, const void *v_p
                          const int32_t *idx, int32_t k_p, void *k_ctx, void *v_ctx,
                          hipStream_t s);
 
+// Where the context keys come from: idx == nullptr means k_ctx / v_ctx are
+// contiguous [n_ctx][H][d] buffers; otherwise they are the pools
+// [max_pages][page_tokens][H][d] and context key n is token n % page_tokens
+// of page idx[n / page_tokens] (n_ctx = k_p * page_tokens).
+struct PagedCtx {
+    const int32_t *idx = nullptr;   // device [k_p]
+    int32_t page_tokens = 0;
+    int32_t max_pages = 0;
+};
+
 hipError_t launch_attention_f32(int32_t n_heads, int32_t head_dim, const float *q, int32_t n_q,
                                 const float *k_ctx, const float *v_ctx, int32_t n_ctx,
                                 const float *k_own, const float *v_own, int32_t n_own,
-                                float scale, float *out, float *lse, hipStream_t s);
+                                float scale, float *out, float *lse, const PagedCtx &pg,
+                                hipStream_t s);
 
 // bf16 attention launch plan: one block per (query block, head) item, or
 // (split) one block per CU, each taking an equal run of the items' key tiles,
@@ -93,6 +104,7 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
                                  const uint16_t *k_ctx, const uint16_t *v_ctx, int32_t n_ctx,
                                  const uint16_t *k_own, const uint16_t *v_own, int32_t n_own,
                                  float scale, int32_t out_dtype, void *out, float *lse,
-                                 const AttnPlan &plan, void *workspace, hipStream_t s);
+                                 const AttnPlan &plan, void *workspace, const PagedCtx &pg,
+                                 hipStream_t s);
 
 }  // namespace wa

@@ -239,3 +239,38 @@ def test_attention_rejects(lib):
     assert _attn(lib, **big) == E                                         # workspace missing
     assert _attn(lib, ws=A, ws_bytes=1024, **big) == E                    # too small
     assert _attn(lib, ws=MIS, ws_bytes=1 << 30, **big) == E               # misaligned
+
+
+def _pattn(lib, lay=None, q=A, n_q=64, kp=A, vp=B, idx=A, k_p=2, ko=A, vo=B, n_own=64,
+           scale=0.1, odt=wa.WA_F32, out=B, lse=NULL, ws=NULL, ws_bytes=0):
+    return lib.wa_paged_attention(lay if lay is not None else L(), q, n_q, kp, vp, idx, k_p, ko,
+                                  vo, n_own, scale, odt, out, lse, ws, ws_bytes, None)
+
+
+def test_paged_attention_rejects(lib):
+    """Every argument rule of wa_paged_attention, one bad argument per call."""
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert lib.wa_paged_attention(None, A, 64, A, B, A, 2, A, B, 64, 0.1, wa.WA_F32, B, NULL,
+                                  NULL, 0, None) == E
+    assert _pattn(lib, kp=NULL) == E
+    assert _pattn(lib, vp=NULL) == E
+    assert _pattn(lib, idx=NULL) == E
+    assert _pattn(lib, idx=ctypes.c_void_p(0x10002)) == E     # int32 alignment
+    assert _pattn(lib, k_p=0) == E
+    assert _pattn(lib, k_p=-3) == E
+    assert _pattn(lib, lay=L(pt=0)) == E
+    assert _pattn(lib, lay=L(pages=0)) == E
+    assert _pattn(lib, k_p=200000) == U                       # k_p * page_tokens overflows
+    assert _pattn(lib, q=NULL) == E
+    assert _pattn(lib, out=NULL) == E
+    assert _pattn(lib, n_q=0) == E
+    assert _pattn(lib, n_own=-1) == E
+    assert _pattn(lib, ko=NULL) == E
+    assert _pattn(lib, kp=MIS) == E
+    assert _pattn(lib, scale=float("nan")) == E
+    assert _pattn(lib, lay=L(d=64)) == U
+    assert _pattn(lib, odt=5) == U
+    big = dict(n_q=1024, k_p=2, n_own=300, odt=wa.WA_BF16)
+    assert lib.wa_attention_workspace_bytes(L(), 1024, 2 * 12480, 300) > 0
+    assert _pattn(lib, **big) == E                           # workspace missing
+    assert _pattn(lib, ws=A, ws_bytes=1024, **big) == E      # too small
