@@ -146,3 +146,21 @@ def test_paged_full_size_workload():
     for j in range(wl.n_pages):
         run.append(j)
     _compare(wl, run, [11, 3, 14, 7], rows=rows_sample(wl.n_q, 12), out_dtypes=[wa.WA_BF16])
+
+
+def test_paged_ids_outside_the_pool_stay_inside_it():
+    """An id outside [0, max_pages) is clamped into the pool before any
+    address is formed (the ABI leaves the result unspecified): the call
+    completes and the output is finite, on both copy paths."""
+    for ft in (64, 50):   # 128-token pages (whole tiles) and 100-token pages (per row)
+        wl = W.scaled(W.WORKLOADS["wan_kp4"], n_heads=2, frame_tokens=ft, page_frames=2,
+                      n_pages=4, chunk_frames=2, k_p=2)
+        run = _pool(wl)
+        q, ko, vo = W.chunk_qkv(wl, 0, 0)
+        idx_d = torch.tensor([-1, 99], dtype=torch.int32, device="cuda")
+        say("paged attention, ids outside the pool", wl.page_tokens)
+        out = wa.wa_paged_attention(run.L, to_device(q), run.k_pool, run.v_pool, idx_d, 2,
+                                    to_device(ko), to_device(vo), wl.softmax_scale,
+                                    out_dtype=wa.WA_F32)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all())
