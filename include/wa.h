@@ -10,6 +10,7 @@
  *   wa_select_pages    score the chunk's mean query against the page mean
  *                      keys and keep the top-K_p pages (optionally after a
  *                      prompt stage that picks the candidate chunks);
+ *   wa_select_window   the most recent pages plus the top-K_p of the rest;
  *   wa_gather          copy the kept pages into one contiguous K/V buffer;
  *   wa_block_attention unmasked softmax attention of the chunk's queries over
  *                      the gathered pages followed by the chunk's own K/V;
@@ -78,6 +79,8 @@ typedef int32_t wa_status;
 #define WA_MAX_ROW_ELEMS 4096
 /* Largest candidate count of one selection (WA_ERR_UNSUPPORTED above). */
 #define WA_MAX_CANDIDATES 4096
+/* Most pages a sliding window (wa_select_window) may hold. */
+#define WA_MAX_WINDOW 64
 
 typedef struct wa_layout {
     int32_t n_heads;     /* H >= 1 */
@@ -166,6 +169,31 @@ wa_status wa_select_pages(const wa_layout *layout, const void *q, int32_t n_q,
                           const wa_prompt_stage *prompt, int32_t k_p, int32_t *out_idx,
                           double *out_scores, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Sliding window plus selective fetch (Inferix summary, "Dual access
+ * patterns": a range of the most recent blocks attended densely, and
+ * specific distant blocks fetched by index for long-range context; the
+ * WorldAttention review's Tab. 7 compares retrieval against keeping the
+ * recent pages):
+ *   out_idx[0 .. n_recent)            = recent[0 .. n_recent)   (range access)
+ *   out_idx[n_recent .. n_recent+k_p) = the k_p candidates ranked first by
+ *                                       (alpha desc, page id asc) among those
+ *                                       whose id is not in recent
+ * with alpha as in wa_select_pages.  recent: device [n_recent] pool slots
+ * (the caller's most recent pages, in the order wanted in the output).
+ * k_p may be 0 (window only) and n_recent 0 (wa_select_pages).  out_idx:
+ * device [n_recent + k_p].  out_scores reports alpha for every candidate,
+ * window pages included.  Other arguments, workspace (wa_select_workspace_
+ * bytes) and errors as wa_select_pages, plus: n_recent < 0, n_recent + k_p
+ * < 1, recent NULL with n_recent > 0 -> WA_ERR_INVALID_ARG; n_recent >
+ * WA_MAX_WINDOW -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_select_window(const wa_layout *layout, const void *q, int32_t n_q,
+                           const double *page_means, const int32_t *cand, int32_t n_cand,
+                           const wa_prompt_stage *prompt, const int32_t *recent,
+                           int32_t n_recent, int32_t k_p, int32_t *out_idx, double *out_scores,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Gather (WorldAttention review, "Core Idea", item 3: the retrieved pages are

@@ -221,6 +221,23 @@ def select_pages(q, page_means, k_p, cand=None, prompt=None):
     return res
 
 
+def select_window(q, page_means, k_p, recent, cand=None, prompt=None):
+    """Sliding window plus selective fetch -- Inferix summary, "Dual access
+    patterns" (range access to the most recent blocks, index-based fetch of
+    distant ones).  The page stage of ``select_pages`` run over the candidates
+    whose id is not in the window; the window's ids come first, in the given
+    order, then the top k_p of the rest; ranks with no candidate left are -1.
+    Returns dict(idx, alpha, cand) with alpha for every candidate."""
+    recent = np.ascontiguousarray(recent, dtype=np.int32)
+    res = select_pages(q, page_means, 0, cand=cand, prompt=prompt)
+    keep = ~np.isin(res["cand"], recent)
+    rest_alpha, rest_ids = res["alpha"][keep], res["cand"][keep]
+    kk = min(int(k_p), rest_ids.size)
+    sel = top_k(rest_alpha, rest_ids, kk)
+    idx = np.concatenate([recent, sel, np.full(int(k_p) - kk, -1, np.int32)]).astype(np.int32)
+    return dict(idx=idx, alpha=res["alpha"], cand=res["cand"])
+
+
 def boundary_margin(alpha: np.ndarray, k_p: int) -> float:
     """Gap between the k_p-th and (k_p+1)-th best score (inf if none)."""
     s = np.sort(np.asarray(alpha, dtype=np.float64))[::-1]

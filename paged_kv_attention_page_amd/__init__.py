@@ -23,8 +23,8 @@ import torch
 __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "WA_F32", "WA_BF16",
            "Layout", "PromptStage", "WaError", "load_library", "library_path", "layout",
            "wa_append_workspace_bytes", "wa_append_page", "wa_select_workspace_bytes",
-           "wa_select_pages", "wa_gather", "wa_attention_workspace_bytes", "wa_block_attention",
-           "wa_paged_attention", "wa_status_string"]
+           "wa_select_pages", "wa_select_window", "wa_gather", "wa_attention_workspace_bytes",
+           "wa_block_attention", "wa_paged_attention", "wa_status_string"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -94,6 +94,8 @@ def load_library():
     lib.wa_select_workspace_bytes.restype = sz
     lib.wa_select_pages.argtypes = [L, p, i32, p, p, i32, P, i32, p, p, p, sz, p]
     lib.wa_select_pages.restype = i32
+    lib.wa_select_window.argtypes = [L, p, i32, p, p, i32, P, p, i32, i32, p, p, p, sz, p]
+    lib.wa_select_window.restype = i32
     lib.wa_gather.argtypes = [L, p, p, p, i32, p, p, p]
     lib.wa_gather.restype = i32
     lib.wa_attention_workspace_bytes.argtypes = [L, i32, i32, i32]
@@ -214,9 +216,8 @@ def wa_select_workspace_bytes(L: Layout, n_q: int, n_cand: int, prompt=None) -> 
         ctypes.byref(L), int(n_q), int(n_cand), ctypes.byref(ps) if ps is not None else None))
 
 
-def wa_select_pages(L: Layout, q, page_means, k_p: int, cand=None, n_cand=None, prompt=None,
-                    out_idx=None, out_scores=None, workspace=None, stream=None):
-    """Top-K_p page ids (device int32 [k_p]) for the chunk's queries q [n_q, H, d]."""
+def _select(L, q, page_means, k_p, cand, n_cand, prompt, recent, out_idx, out_scores, workspace,
+            stream, where):
     lib = load_library()
     _need(q, "q", L.torch_dtype)
     n_q = q.numel() // L.row_elems
@@ -232,20 +233,46 @@ def wa_select_pages(L: Layout, q, page_means, k_p: int, cand=None, n_cand=None, 
         _need(cand, "cand", torch.int32, n_cand)
     elif n_cand is None:
         n_cand = L.max_pages
+    n_recent = 0
+    if recent is not None:
+        _need(recent, "recent", torch.int32)
+        n_recent = recent.numel()
+    n_out = n_recent + int(k_p)
     if out_idx is None:
-        out_idx = torch.empty(max(int(k_p), 1), dtype=torch.int32, device=q.device)
-    _need(out_idx, "out_idx", torch.int32, k_p)
+        out_idx = torch.empty(max(n_out, 1), dtype=torch.int32, device=q.device)
+    _need(out_idx, "out_idx", torch.int32, n_out)
     if out_scores is not None:
         _need(out_scores, "out_scores", torch.float64, n_cand)
     nbytes = lib.wa_select_workspace_bytes(ctypes.byref(L), int(n_q), int(n_cand),
                                            ctypes.byref(ps) if ps is not None else None)
     ws = _workspace(nbytes, workspace, q)
-    st = lib.wa_select_pages(ctypes.byref(L), _ptr(q), int(n_q), _ptr(page_means), _ptr(cand),
-                             int(n_cand), ctypes.byref(ps) if ps is not None else None, int(k_p),
-                             _ptr(out_idx), _ptr(out_scores), _ptr(ws), ws.numel(),
-                             _stream(stream))
-    _check(st, "wa_select_pages")
+    pst = ctypes.byref(ps) if ps is not None else None
+    if where == "wa_select_pages":
+        st = lib.wa_select_pages(ctypes.byref(L), _ptr(q), int(n_q), _ptr(page_means), _ptr(cand),
+                                 int(n_cand), pst, int(k_p), _ptr(out_idx), _ptr(out_scores),
+                                 _ptr(ws), ws.numel(), _stream(stream))
+    else:
+        st = lib.wa_select_window(ctypes.byref(L), _ptr(q), int(n_q), _ptr(page_means),
+                                  _ptr(cand), int(n_cand), pst, _ptr(recent), int(n_recent),
+                                  int(k_p), _ptr(out_idx), _ptr(out_scores), _ptr(ws),
+                                  ws.numel(), _stream(stream))
+    _check(st, where)
     return out_idx
+
+
+def wa_select_pages(L: Layout, q, page_means, k_p: int, cand=None, n_cand=None, prompt=None,
+                    out_idx=None, out_scores=None, workspace=None, stream=None):
+    """Top-K_p page ids (device int32 [k_p]) for the chunk's queries q [n_q, H, d]."""
+    return _select(L, q, page_means, k_p, cand, n_cand, prompt, None, out_idx, out_scores,
+                   workspace, stream, "wa_select_pages")
+
+
+def wa_select_window(L: Layout, q, page_means, recent, k_p: int, cand=None, n_cand=None,
+                     prompt=None, out_idx=None, out_scores=None, workspace=None, stream=None):
+    """The pages of `recent` (device int32, the sliding window) followed by the
+    top-K_p of the other candidates: device int32 [len(recent) + k_p]."""
+    return _select(L, q, page_means, k_p, cand, n_cand, prompt, recent, out_idx, out_scores,
+                   workspace, stream, "wa_select_window")
 
 
 def wa_gather(L: Layout, k_pool, v_pool, idx, k_p: int, k_ctx=None, v_ctx=None, stream=None):

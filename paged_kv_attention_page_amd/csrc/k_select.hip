@@ -219,14 +219,27 @@ __global__ __launch_bounds__(kStage2Threads) void k_select_stage2(const double *
 
 }
 
-// One block of kStage3Threads threads.
+// One block of kStage3Threads threads.  With a sliding window (n_recent > 0,
+// Inferix summary, "Dual access patterns": range access to the most recent
+// pages plus index-based selective fetch), the window's ids are written
+// first and take no part in the ranking, which fills the k_p entries after
+// them; their scores are still reported.
 __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
     const double *__restrict__ alpha_part, int groups, int n_cand,
     const int32_t *__restrict__ cand_ws, int max_pages, double sqrt_d, int k_p,
+    const int32_t *__restrict__ recent, int n_recent,
     int32_t *__restrict__ out_idx, double *__restrict__ out_scores) {
     __shared__ double sc[WA_MAX_CANDIDATES];
     __shared__ int ids[WA_MAX_CANDIDATES];
+    __shared__ int win[WA_MAX_WINDOW];
     const int t = threadIdx.x;
+    for (int r = t; r < n_recent; r += blockDim.x) {
+        const int id = recent[r];
+        win[r] = id;
+        out_idx[r] = id;
+    }
+    __syncthreads();
+    out_idx += n_recent;
     // alpha_j: group partials added in group order; an id outside the pool
     // scores -inf and is never selected
     for (int j = t; j < n_cand; j += blockDim.x) {
@@ -243,8 +256,10 @@ __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
         const int id = cand_ws[j];
         const bool valid = id >= 0 && id < max_pages;
         const double s = valid ? v / sqrt_d : -INFINITY;
+        bool in_window = false;
+        for (int w = 0; w < n_recent; ++w) in_window |= win[w] == id;
         sc[j] = s;
-        ids[j] = valid ? id : -1;
+        ids[j] = valid && !in_window ? id : -1;
         if (out_scores) out_scores[j] = s;
     }
     __syncthreads();
@@ -294,8 +309,8 @@ __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
 
 hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const double *page_means,
                          const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
-                         int32_t k_p, int32_t *out_idx, double *out_scores, void *ws,
-                         hipStream_t s) {
+                         const int32_t *recent, int32_t n_recent, int32_t k_p, int32_t *out_idx,
+                         double *out_scores, void *ws, hipStream_t s) {
     const int64_t hd = (int64_t)L.n_heads * L.head_dim;
     const int n_chunks = prompt ? prompt->n_chunks : 0;
     const SelectWs w = select_workspace(L.dtype, hd, n_q, n_cand, n_chunks);
@@ -335,7 +350,8 @@ hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const d
 
     hipLaunchKernelGGL(k_select_stage3, dim3(1), dim3(kStage3Threads), 0, s,
                        (const double *)alpha_part, w.groups, n_cand, (const int32_t *)cand_ws,
-                       L.max_pages, sqrt((double)L.head_dim), k_p, out_idx, out_scores);
+                       L.max_pages, sqrt((double)L.head_dim), k_p, recent, n_recent, out_idx,
+                       out_scores);
     return hipGetLastError();
 }
 

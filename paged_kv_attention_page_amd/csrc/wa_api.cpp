@@ -77,24 +77,50 @@ size_t wa_select_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_cand
         .total;
 }
 
-wa_status wa_select_pages(const wa_layout *L, const void *q, int32_t n_q, const double *page_means,
-                          const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
-                          int32_t k_p, int32_t *out_idx, double *out_scores, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+namespace {
+
+// Shared by wa_select_pages (no window) and wa_select_window.
+wa_status select_impl(const wa_layout *L, const void *q, int32_t n_q, const double *page_means,
+                      const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
+                      const int32_t *recent, int32_t n_recent, int32_t k_p, int32_t *out_idx,
+                      double *out_scores, void *workspace, size_t workspace_bytes,
+                      void *stream) {
     wa_status st = check_layout(L, true);
     if (st != WA_OK) return st;
     if (!q || !page_means || !out_idx || !workspace) return WA_ERR_INVALID_ARG;
-    if (n_q < 1 || n_cand < 1 || k_p < 1 || k_p > n_cand) return WA_ERR_INVALID_ARG;
-    if (n_cand > WA_MAX_CANDIDATES) return WA_ERR_UNSUPPORTED;
+    if (n_q < 1 || n_cand < 1 || k_p < 0 || k_p > n_cand) return WA_ERR_INVALID_ARG;
+    if (n_recent < 0 || n_recent + k_p < 1 || (n_recent > 0 && !recent)) return WA_ERR_INVALID_ARG;
+    if (n_cand > WA_MAX_CANDIDATES || n_recent > WA_MAX_WINDOW) return WA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(page_means) || !aligned16(out_idx) || !aligned16(workspace) ||
-        (cand && !aligned16(cand)) || (out_scores && !aligned16(out_scores)))
+        (cand && !aligned16(cand)) || (out_scores && !aligned16(out_scores)) ||
+        ((uintptr_t)recent & 3u))
         return WA_ERR_INVALID_ARG;
     st = check_prompt(L, prompt, cand, n_cand);
     if (st != WA_OK) return st;
     if (workspace_bytes < wa_select_workspace_bytes(L, n_q, n_cand, prompt))
         return WA_ERR_INVALID_ARG;
-    return from_hip(launch_select(*L, q, n_q, page_means, cand, n_cand, prompt, k_p, out_idx,
-                                  out_scores, workspace, (hipStream_t)stream));
+    return from_hip(launch_select(*L, q, n_q, page_means, cand, n_cand, prompt, recent, n_recent,
+                                  k_p, out_idx, out_scores, workspace, (hipStream_t)stream));
+}
+
+}  // namespace
+
+wa_status wa_select_pages(const wa_layout *L, const void *q, int32_t n_q, const double *page_means,
+                          const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
+                          int32_t k_p, int32_t *out_idx, double *out_scores, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (k_p < 1) return WA_ERR_INVALID_ARG;
+    return select_impl(L, q, n_q, page_means, cand, n_cand, prompt, nullptr, 0, k_p, out_idx,
+                       out_scores, workspace, workspace_bytes, stream);
+}
+
+wa_status wa_select_window(const wa_layout *L, const void *q, int32_t n_q,
+                           const double *page_means, const int32_t *cand, int32_t n_cand,
+                           const wa_prompt_stage *prompt, const int32_t *recent,
+                           int32_t n_recent, int32_t k_p, int32_t *out_idx, double *out_scores,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    return select_impl(L, q, n_q, page_means, cand, n_cand, prompt, recent, n_recent, k_p,
+                       out_idx, out_scores, workspace, workspace_bytes, stream);
 }
 
 wa_status wa_gather(const wa_layout *L, const void *k_pool, const void *v_pool, const int32_t *idx,

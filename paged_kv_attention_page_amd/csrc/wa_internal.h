@@ -60,10 +60,13 @@ hipError_t launch_append(const wa_layout &L, const void *k_src, const void *v_sr
                          void *v_pool, int32_t slot, double *page_means, void *ws,
                          hipStream_t s);
 
+// recent / n_recent: the sliding window (range access); its ids come first in
+// out_idx and are excluded from the ranked (selective) part, which fills
+// out_idx[n_recent .. n_recent + k_p).  n_recent = 0: the plain page stage.
 hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const double *page_means,
                          const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
-                         int32_t k_p, int32_t *out_idx, double *out_scores, void *ws,
-                         hipStream_t s);
+                         const int32_t *recent, int32_t n_recent, int32_t k_p, int32_t *out_idx,
+                         double *out_scores, void *ws, hipStream_t s);
 
 hipError_t launch_gather(const wa_layout &L, const void *k_pool, const void *v_pool,
                          const int32_t *idx, int32_t k_p, void *k_ctx, void *v_ctx,

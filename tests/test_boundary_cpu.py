@@ -152,6 +152,29 @@ def test_select_rejects(lib):
     assert _select(lib, lay=L(pages=0)) == E
 
 
+def _window(lib, lay=None, q=A, n_q=100, means=A, cand=NULL, n_cand=16, recent=B, n_recent=2,
+            k_p=4, out=A, ws=A, wsb=1 << 40):
+    return lib.wa_select_window(lay if lay is not None else L(), q, n_q, means, cand, n_cand,
+                                None, recent, n_recent, k_p, out, None, ws, wsb, None)
+
+
+def test_select_window_rejects(lib):
+    """The window's own rules, one bad argument per call (the rest of the
+    page-stage rules are shared with wa_select_pages)."""
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert _window(lib, recent=NULL) == E                    # n_recent > 0 needs the ids
+    assert _window(lib, n_recent=-1) == E
+    assert _window(lib, n_recent=0, k_p=0) == E              # nothing to select
+    assert _window(lib, k_p=-1) == E
+    assert _window(lib, k_p=17) == E                         # more than the candidates
+    assert _window(lib, recent=ctypes.c_void_p(0x20002)) == E
+    assert _window(lib, n_recent=65) == U                    # over WA_MAX_WINDOW
+    assert _window(lib, q=NULL) == E
+    assert _window(lib, ws=NULL) == E
+    assert _window(lib, wsb=16) == E
+    assert _window(lib, lay=L(pages=0)) == E
+
+
 def _prompt(n_chunks=16, emb=4096, ppc=4, keep=4):
     return wa.PromptStage(0x30000, 0x40000, 0x50000, n_chunks, emb, ppc, keep, None, None)
 

@@ -126,6 +126,70 @@ def test_top_k_all_returns_every_id(oracle_lib):
 
 
 # ----------------------------------------------------------------------------
+# sliding window plus selective fetch (Inferix summary, "Dual access patterns")
+
+def _constant_pool(values, H=2, d=8):
+    """Page j's keys all equal values[j]: its mean is values[j] everywhere."""
+    return np.stack([np.full((H, d), v, dtype=np.float64) for v in values])
+
+
+def test_window_closed_form_on_constant_pages(oracle_lib):
+    """With q = 1 everywhere, alpha_j = values[j] * H * d / sqrt(d), so the
+    ranking is the order of values: 5, 1, 3, 7, 4, 0, 6, 2.  The window keeps
+    its own order, its best page (5) is not fetched again, and the fetched
+    pages are the next best outside the window."""
+    values = [0.3, 2.0, -1.0, 1.5, 0.7, 2.5, 0.1, 1.2]
+    means = _constant_pool(values)
+    q = np.ones((4, 2, 8), dtype=np.float32)
+    got = oracle_lib.select_window(q, means, 3, [6, 5])
+    assert got["idx"].tolist() == [6, 5, 1, 3, 7]
+    assert np.allclose(got["alpha"], np.array(values) * 2 * 8 / math.sqrt(8))
+    assert oracle_lib.select_window(q, means, 0, [2, 0])["idx"].tolist() == [2, 0]
+    assert oracle_lib.select_window(q, means, 2, [])["idx"].tolist() == [5, 1]
+
+
+def test_window_empty_is_the_page_stage(oracle_lib):
+    means = RNG.standard_normal((9, 2, 8))
+    q = f32(5, 2, 8)
+    for k in (1, 4, 9):
+        assert (oracle_lib.select_window(q, means, k, [])["idx"].tolist()
+                == oracle_lib.select_pages(q, means, k)["idx"].tolist())
+
+
+@pytest.mark.parametrize("n,w,k", [(7, 2, 3), (8, 3, 2), (6, 1, 5), (9, 4, 1)])
+def test_window_fetch_is_the_best_subset_outside_the_window(oracle_lib, n, w, k):
+    for trial in range(4):
+        means = RNG.standard_normal((n, 2, 8))
+        q = f32(3, 2, 8)
+        window = RNG.permutation(n)[:w].astype(np.int32)
+        res = oracle_lib.select_window(q, means, k, window)
+        idx, alpha = res["idx"], res["alpha"]
+        assert idx[:w].tolist() == window.tolist()
+        rest = [j for j in range(n) if j not in set(window.tolist())]
+        kk = min(k, len(rest))
+        best = max(itertools.combinations(rest, kk), key=lambda s: sum(alpha[j] for j in s))
+        assert set(idx[w:w + kk].tolist()) == set(best)
+        assert idx[w + kk:].tolist() == [-1] * (k - kk)
+        s_out = [alpha[j] for j in idx[w:w + kk]]
+        assert all(a > b for a, b in zip(s_out, s_out[1:]))
+
+
+def test_window_covering_every_candidate_fetches_nothing(oracle_lib):
+    means = RNG.standard_normal((4, 2, 8))
+    q = f32(3, 2, 8)
+    got = oracle_lib.select_window(q, means, 2, [3, 1, 0, 2])
+    assert got["idx"].tolist() == [3, 1, 0, 2, -1, -1]
+
+
+def test_window_order_only_moves_the_window(oracle_lib):
+    means = RNG.standard_normal((10, 2, 8))
+    q = f32(3, 2, 8)
+    a = oracle_lib.select_window(q, means, 3, [7, 2, 9])["idx"]
+    b = oracle_lib.select_window(q, means, 3, [9, 7, 2])["idx"]
+    assert b[:3].tolist() == [9, 7, 2] and a[3:].tolist() == b[3:].tolist()
+
+
+# ----------------------------------------------------------------------------
 # prompt stage
 
 def test_cosine_closed_forms(oracle_lib):
