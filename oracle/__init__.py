@@ -238,6 +238,103 @@ def select_window(q, page_means, k_p, recent, cand=None, prompt=None):
     return dict(idx=idx, alpha=res["alpha"], cand=res["cand"])
 
 
+# ----------------------------------------------------------------------------
+# HSA sparse branch (WorldAttention review, "HSA: Dual Branches of Linear +
+# Sparse"): block-level selection with a pooled attention map, a per-head
+# cumulative-mass threshold, attention over the selected blocks only.  The
+# readings taken where the page is silent (query pooling per 256-query block,
+# an unweighted softmax over block means, tau_h given per head because the
+# Gini-to-threshold formula did not survive extraction) are listed with the
+# build's design notes.
+
+def _widen(x) -> np.ndarray:
+    """Input encoding (float32, or bf16 patterns as uint16) -> float64, exactly."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def hsa_key_blocks(n_ctx: int, n_own: int, b_inter: int = 128, b_intra: int = 64):
+    """[start, end) of every key block in [ctx ++ own] key order: the context
+    (past pages) in blocks of b_inter keys, the chunk's own keys in blocks of
+    b_intra; a last block may be shorter."""
+    blocks = [(s, min(s + b_inter, n_ctx)) for s in range(0, n_ctx, b_inter)]
+    blocks += [(n_ctx + s, n_ctx + min(s + b_intra, n_own)) for s in range(0, n_own, b_intra)]
+    return blocks
+
+
+def gini(p) -> float:
+    """Gini coefficient sum_i sum_j |p_i - p_j| / (2 n sum_i p_i) of a
+    non-negative distribution."""
+    p = np.asarray(p, dtype=np.float64)
+    return float(np.abs(p[:, None] - p[None, :]).sum() / (2.0 * p.size * p.sum()))
+
+
+def select_blocks(mass, tau: float):
+    """The fewest blocks whose mass reaches tau: blocks taken in decreasing mass
+    (ties to the lower index) until the running sum is >= tau, at least one;
+    returned in ascending (key) order."""
+    order = sorted(range(len(mass)), key=lambda j: (-float(mass[j]), j))
+    total, chosen = 0.0, []
+    for j in order:
+        chosen.append(j)
+        total += float(mass[j])
+        if total >= tau:
+            break
+    return sorted(chosen)
+
+
+def hsa_pooled_map(q_rows, k_all, blocks, scale: float) -> np.ndarray:
+    """Pooled attention map of one query block for every head: softmax over key
+    blocks of (mean query . mean key of the block) * scale.  q_rows
+    [n, H, d], k_all [n_keys, H, d] (input encoding); returns [H, n_blocks]."""
+    qbar = _widen(q_rows).mean(axis=0)                          # [H, d]
+    k = _widen(k_all)
+    kbar = np.stack([k[a:b].mean(axis=0) for a, b in blocks])  # [nb, H, d]
+    s = np.einsum("hd,jhd->hj", qbar, kbar) * scale
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def hsa_sparse(q, k_ctx, v_ctx, k_own, v_own, scale: float, tau, q_block: int = 256,
+               b_inter: int = 128, b_intra: int = 64, rows=None):
+    """Sparse branch: for each head h and query block b (q_block queries), the
+    key blocks chosen by select_blocks(pooled map row, tau[h]); each query of
+    the block attends (one softmax, no mask) over the keys of those blocks in
+    key order.  Returns dict(out [n_rows, H, d], lse [H, n_rows], sel
+    {(h, b): block list}, gini {(h, b): G}, blocks)."""
+    q = np.ascontiguousarray(q)
+    n_heads = q.shape[1]
+    n_ctx = 0 if k_ctx is None else k_ctx.shape[0]
+    n_own = 0 if k_own is None else k_own.shape[0]
+    parts_k = [x for x in (k_ctx, k_own) if x is not None and x.shape[0]]
+    parts_v = [x for x in (v_ctx, v_own) if x is not None and x.shape[0]]
+    k_all, v_all = np.concatenate(parts_k), np.concatenate(parts_v)
+    blocks = hsa_key_blocks(n_ctx, n_own, b_inter, b_intra)
+    if rows is None:
+        rows = np.arange(q.shape[0], dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, n_heads, q.shape[2]), dtype=np.float64)
+    lse = np.empty((n_heads, rows.size), dtype=np.float64)
+    sel, gin = {}, {}
+    for b in sorted(set((rows // q_block).tolist())):
+        lo, hi = b * q_block, min((b + 1) * q_block, q.shape[0])
+        pmap = hsa_pooled_map(q[lo:hi], k_all, blocks, scale)
+        mine = np.nonzero(rows // q_block == b)[0]
+        for h in range(n_heads):
+            chosen = select_blocks(pmap[h], float(tau[h]))
+            sel[(h, b)], gin[(h, b)] = chosen, gini(pmap[h])
+            keys = np.concatenate([np.arange(blocks[j][0], blocks[j][1]) for j in chosen])
+            kh = np.ascontiguousarray(k_all[keys][:, h:h + 1])
+            vh = np.ascontiguousarray(v_all[keys][:, h:h + 1])
+            o, l = attention(np.ascontiguousarray(q[:, h:h + 1]), kh, vh, None, None, scale,
+                             rows=rows[mine])
+            out[mine, h] = o[:, 0]
+            lse[h, mine] = l[0]
+    return dict(out=out, lse=lse, sel=sel, gini=gin, blocks=blocks)
+
+
 def boundary_margin(alpha: np.ndarray, k_p: int) -> float:
     """Gap between the k_p-th and (k_p+1)-th best score (inf if none)."""
     s = np.sort(np.asarray(alpha, dtype=np.float64))[::-1]

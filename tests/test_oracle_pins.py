@@ -358,3 +358,92 @@ def test_tiny_workload_selection_has_a_clear_margin(oracle_lib):
     sel = oracle_lib.select_pages(q, means, wl.k_p)
     margin = oracle_lib.boundary_margin(sel["alpha"], wl.k_p)
     assert margin > 1e-6 * np.abs(sel["alpha"]).max()
+
+
+# ----------------------------------------------------------------------------
+# HSA sparse branch (WorldAttention review, "HSA: Dual Branches of Linear +
+# Sparse"): key blocks, pooled map, Gini coefficient, cumulative-mass
+# selection, attention over the selected blocks
+
+def test_gini_closed_forms(oracle_lib):
+    assert oracle_lib.gini(np.full(6, 0.25)) == 0.0
+    assert abs(oracle_lib.gini([0, 0, 1.0, 0, 0]) - 4 / 5) < 1e-15      # one-hot: (n-1)/n
+    assert abs(oracle_lib.gini([1.0, 3.0]) - 0.25) < 1e-15               # |1-3|*2 / (2*2*4)
+    p = RNG.random(9)
+    assert abs(oracle_lib.gini(p) - oracle_lib.gini(7.5 * p)) < 1e-14    # scale invariant
+
+
+@pytest.mark.parametrize("n", [5, 7, 8])
+def test_select_blocks_is_the_fewest_by_brute_force(oracle_lib, n):
+    for trial in range(6):
+        mass = RNG.random(n)
+        mass /= mass.sum()
+        tau = float(RNG.uniform(0.05, 0.95))
+        got = oracle_lib.select_blocks(mass, tau)
+        m = len(got)
+        reach = [k for k in range(1, n + 1)
+                 if any(sum(mass[j] for j in s) >= tau for s in itertools.combinations(range(n), k))]
+        assert m == min(reach)
+        best = max(itertools.combinations(range(n), m), key=lambda s: sum(mass[j] for j in s))
+        assert got == sorted(best)
+    mass = np.array([0.1, 0.5, 0.2, 0.2])
+    assert oracle_lib.select_blocks(mass, 0.3) == [1]                    # the largest alone
+    assert oracle_lib.select_blocks(mass, 2.0) == [0, 1, 2, 3]            # unreachable: all
+    assert oracle_lib.select_blocks(mass, 0.7) == [1, 2]                  # tie 0.2/0.2 -> lower index
+
+
+def test_key_blocks_cover_every_key_once(oracle_lib):
+    got = oracle_lib.hsa_key_blocks(300, 130)
+    assert got == [(0, 128), (128, 256), (256, 300), (300, 364), (364, 428), (428, 430)]
+    assert oracle_lib.hsa_key_blocks(0, 64) == [(0, 64)]
+
+
+def test_pooled_map_closed_form(oracle_lib):
+    """Keys of block j all equal c_j e, queries all equal a e: the block means
+    are c_j e and a e, so the map row is softmax_j(a c_j |e|^2 scale)."""
+    d, H = 8, 2
+    e = np.arange(1, d + 1, dtype=np.float32) / 8
+    c = [0.5, -1.0, 2.0, 0.25]
+    blocks = oracle_lib.hsa_key_blocks(3 * 16, 16, b_inter=16, b_intra=16)
+    k = np.concatenate([np.tile(cj * e, (16, H, 1)) for cj in c]).astype(np.float32)
+    q = np.tile(0.75 * e, (5, H, 1)).astype(np.float32)
+    got = oracle_lib.hsa_pooled_map(q, k, blocks, 0.3)
+    s = np.array([0.75 * cj * float(e @ e) * 0.3 for cj in c])
+    want = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+    assert np.allclose(got, np.tile(want, (H, 1)), rtol=1e-12, atol=0)
+
+
+def _hsa_inputs(n_q=300, n_ctx=384, n_own=140, H=2, d=16):
+    return f32(n_q, H, d), f32(n_ctx, H, d), f32(n_ctx, H, d), f32(n_own, H, d), f32(n_own, H, d)
+
+
+def test_hsa_every_block_is_dense_attention(oracle_lib):
+    q, kc, vc, ko, vo = _hsa_inputs()
+    r = oracle_lib.hsa_sparse(q, kc, vc, ko, vo, 0.25, [2.0, 2.0])
+    dense, lse = oracle_lib.attention(q, kc, vc, ko, vo, 0.25)
+    assert all(len(v) == len(r["blocks"]) for v in r["sel"].values())
+    assert np.array_equal(r["out"], dense) and np.array_equal(r["lse"], lse)
+
+
+def test_hsa_one_block_is_softmax_over_its_keys(oracle_lib):
+    """tau below every mass keeps one block: the map's argmax; each row is then
+    the textbook softmax over that block's keys (numpy, fp64)."""
+    q, kc, vc, ko, vo = _hsa_inputs()
+    scale = 0.25
+    rows = np.array([0, 17, 255, 256, 299])
+    r = oracle_lib.hsa_sparse(q, kc, vc, ko, vo, scale, [1e-12, 1e-12], rows=rows)
+    k_all = np.concatenate([kc, ko]).astype(np.float64)
+    v_all = np.concatenate([vc, vo]).astype(np.float64)
+    for i, row in enumerate(rows):
+        b = row // 256
+        for h in range(2):
+            (j,) = r["sel"][(h, b)]
+            pmap = oracle_lib.hsa_pooled_map(q[b * 256:(b + 1) * 256], np.concatenate([kc, ko]),
+                                             r["blocks"], scale)
+            assert j == int(np.argmax(pmap[h]))
+            a, z = r["blocks"][j]
+            s = k_all[a:z, h] @ q[row, h].astype(np.float64) * scale
+            p = np.exp(s - s.max())
+            want = (p[:, None] * v_all[a:z, h]).sum(axis=0) / p.sum()
+            assert np.abs(r["out"][i, h] - want).max() < 1e-12
+            assert abs(r["lse"][h, i] - (s.max() + np.log(p.sum()))) < 1e-12
