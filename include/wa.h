@@ -15,7 +15,11 @@
  *   wa_block_attention unmasked softmax attention of the chunk's queries over
  *                      the gathered pages followed by the chunk's own K/V;
  *   wa_paged_attention the same attention reading the kept pages in place
- *                      from the pool (no gathered copy).
+ *                      from the pool (no gathered copy);
+ *   wa_hsa_select      the sparse branch's block selection: per head and
+ *                      query block, the fewest key blocks that hold a given
+ *                      share of a pooled attention map;
+ *   wa_sparse_attention attention over those blocks only.
  *
  * Sources (page title, section):
  *   WorldAttention review, "WorldAttention: An Efficient Attention
@@ -81,6 +85,14 @@ typedef int32_t wa_status;
 #define WA_MAX_CANDIDATES 4096
 /* Most pages a sliding window (wa_select_window) may hold. */
 #define WA_MAX_WINDOW 64
+/* Sparse branch (wa_hsa_select, wa_sparse_attention): keys per context
+ * block, keys per own block, queries per pooled query block, and limits. */
+#define WA_HSA_CTX_BLOCK 128
+#define WA_HSA_OWN_BLOCK 64
+#define WA_HSA_Q_BLOCK 256
+#define WA_MAX_HSA_BLOCKS 2048   /* key blocks of one selection */
+#define WA_HSA_MAX_HEAD_DIM 256  /* head_dim of a selection */
+#define WA_MAX_SPARSE_TILES 4096 /* 64-key tiles of one sparse attention */
 
 typedef struct wa_layout {
     int32_t n_heads;     /* H >= 1 */
@@ -278,6 +290,85 @@ wa_status wa_paged_attention(const wa_layout *layout, const void *q, int32_t n_q
                              int32_t k_p, const void *k_own, const void *v_own, int32_t n_own,
                              float softmax_scale, int32_t out_dtype, void *out, float *lse,
                              void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Bytes of device workspace wa_hsa_select needs (0 if the arguments are
+ * invalid).  Contents need no initialisation.
+ */
+size_t wa_hsa_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ctx,
+                              int32_t n_own);
+
+/*
+ * Sparse branch, block selection (WorldAttention review, "HSA: Dual Branches
+ * of Linear + Sparse": keys in blocks of 128 for the retrieved pages and 64
+ * for the current chunk; a pooled attention map picks, per head, the fewest
+ * blocks whose cumulative attention mass reaches tau_h, whose sparsity the
+ * page measures with the Gini coefficient).  Key blocks, in [ctx ++ own]
+ * order: context keys [128 j, 128 j + 128) (the last may hold 64), then own
+ * keys [64 j, 64 j + 64) (the last may be shorter).  Query block b = queries
+ * [256 b, 256 b + 256).  For head h and query block b, in fp64:
+ *   qbar[c]   = mean over the block's queries of q[i][h][c]
+ *   kbar_j[c] = mean over block j's keys of k[n][h][c]
+ *   p_j       = softmax_j((qbar . kbar_j) * scale)
+ *   G         = sum_i sum_j |p_i - p_j| / (2 nb sum_j p_j)       (Gini)
+ *   selected  = the first m blocks in (p desc, block asc) order, m the least
+ *               count whose running sum (in that order) is >= tau[h], m >= 1
+ *               (all blocks when the sum never reaches tau[h]).
+ * Output per item = h * q_blocks + b (q_blocks = ceil(n_q / 256)):
+ *   sel_count[item]                     tiles selected
+ *   sel_tiles[item * n_tiles + 0 ..)    the selected blocks' 64-key tiles of
+ *                                       [ctx ++ own], ascending (context
+ *                                       block j: tiles 2j, 2j+1; own block j:
+ *                                       tile n_ctx / 64 + j)
+ *   gini[item]                          G (if gini is not NULL)
+ * with n_tiles = ceil((n_ctx + n_own) / 64): exactly the lists
+ * wa_sparse_attention reads.
+ *
+ * q: [n_q][H][d]; k_ctx: [n_ctx][H][d]; k_own: [n_own][H][d] (layout.dtype;
+ * V is not read).  tau: device [H] double.  sel_tiles: device int32
+ * [q_blocks * H][n_tiles]; sel_count: device int32 [q_blocks * H]; gini:
+ * device double [q_blocks * H] or NULL.  scale: the score scale (the
+ * attention's softmax_scale).  workspace: device, >= wa_hsa_workspace_bytes
+ * bytes, 16-byte aligned; calls in flight at once need separate workspaces.
+ * Errors: NULL layout / q / tau / sel_tiles / sel_count / workspace, NULL
+ * pointer of a non-empty segment, n_q < 1, n_ctx < 0, n_own < 0,
+ * n_ctx + n_own < 1, scale not finite and > 0, misaligned pointers,
+ * workspace too small -> WA_ERR_INVALID_ARG; n_ctx not a multiple of 64,
+ * head_dim > WA_HSA_MAX_HEAD_DIM, more than WA_MAX_HSA_BLOCKS key blocks,
+ * unsupported layout -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_hsa_select(const wa_layout *layout, const void *q, int32_t n_q, const void *k_ctx,
+                        int32_t n_ctx, const void *k_own, int32_t n_own, double scale,
+                        const double *tau, int32_t *sel_tiles, int32_t *sel_count, double *gini,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sparse branch, attention over the selected blocks (WorldAttention review,
+ * "HSA: Dual Branches of Linear + Sparse"): for head h and query row i of
+ * query block b = i / 256, item = h * q_blocks + b, the keys n run over the
+ * 64-key tiles sel_tiles[item * n_tiles + 0 .. sel_count[item]) of
+ * [ctx ++ own] (tile t = keys [64 t, 64 t + 64), cut at n_ctx + n_own), in
+ * list order:
+ *   out[i][h] = sum_n exp(s_n) v_n[h] / sum_n exp(s_n),  lse[h][i] = log(sum_n exp(s_n))
+ * with s_n as in wa_block_attention: one softmax, no mask.  Over the full list
+ * 0 .. n_tiles-1 this is wa_block_attention.
+ *
+ * sel_tiles / sel_count: as written by wa_hsa_select, or any lists with
+ * 1 <= count <= n_tiles and strictly ascending entries in [0, n_tiles)
+ * (a count or an entry outside its range is clamped so that every access
+ * stays inside the keys, and the result is then unspecified).  Other
+ * arguments as wa_block_attention; layout.dtype must be WA_BF16 and head_dim
+ * 128.  No workspace: every (query block, head) runs in one workgroup.
+ * Errors: as wa_block_attention, plus NULL or misaligned sel_tiles /
+ * sel_count -> WA_ERR_INVALID_ARG; a WA_F32 layout, more than
+ * WA_MAX_SPARSE_TILES tiles -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_sparse_attention(const wa_layout *layout, const void *q, int32_t n_q,
+                              const void *k_ctx, const void *v_ctx, int32_t n_ctx,
+                              const void *k_own, const void *v_own, int32_t n_own,
+                              float softmax_scale, const int32_t *sel_tiles,
+                              const int32_t *sel_count, int32_t out_dtype, void *out,
+                              float *lse, void *stream);
 
 /* Static text describing a status code. */
 const char *wa_status_string(wa_status status);

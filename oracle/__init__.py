@@ -303,7 +303,8 @@ def hsa_sparse(q, k_ctx, v_ctx, k_own, v_own, scale: float, tau, q_block: int = 
     key blocks chosen by select_blocks(pooled map row, tau[h]); each query of
     the block attends (one softmax, no mask) over the keys of those blocks in
     key order.  Returns dict(out [n_rows, H, d], lse [H, n_rows], sel
-    {(h, b): block list}, gini {(h, b): G}, blocks)."""
+    {(h, b): block list}, gini {(h, b): G}, maps {b: pooled map [H, nb]},
+    blocks)."""
     q = np.ascontiguousarray(q)
     n_heads = q.shape[1]
     n_ctx = 0 if k_ctx is None else k_ctx.shape[0]
@@ -317,10 +318,11 @@ def hsa_sparse(q, k_ctx, v_ctx, k_own, v_own, scale: float, tau, q_block: int = 
     rows = np.asarray(rows, dtype=np.int64)
     out = np.empty((rows.size, n_heads, q.shape[2]), dtype=np.float64)
     lse = np.empty((n_heads, rows.size), dtype=np.float64)
-    sel, gin = {}, {}
+    sel, gin, maps = {}, {}, {}
     for b in sorted(set((rows // q_block).tolist())):
         lo, hi = b * q_block, min((b + 1) * q_block, q.shape[0])
         pmap = hsa_pooled_map(q[lo:hi], k_all, blocks, scale)
+        maps[b] = pmap
         mine = np.nonzero(rows // q_block == b)[0]
         for h in range(n_heads):
             chosen = select_blocks(pmap[h], float(tau[h]))
@@ -332,7 +334,7 @@ def hsa_sparse(q, k_ctx, v_ctx, k_own, v_own, scale: float, tau, q_block: int = 
                              rows=rows[mine])
             out[mine, h] = o[:, 0]
             lse[h, mine] = l[0]
-    return dict(out=out, lse=lse, sel=sel, gini=gin, blocks=blocks)
+    return dict(out=out, lse=lse, sel=sel, gini=gin, maps=maps, blocks=blocks)
 
 
 def boundary_margin(alpha: np.ndarray, k_p: int) -> float:

@@ -24,7 +24,8 @@ __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "W
            "Layout", "PromptStage", "WaError", "load_library", "library_path", "layout",
            "wa_append_workspace_bytes", "wa_append_page", "wa_select_workspace_bytes",
            "wa_select_pages", "wa_select_window", "wa_gather", "wa_attention_workspace_bytes",
-           "wa_block_attention", "wa_paged_attention", "wa_status_string"]
+           "wa_block_attention", "wa_paged_attention", "hsa_shape", "wa_hsa_workspace_bytes",
+           "wa_hsa_select", "wa_sparse_attention", "wa_status_string"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -105,6 +106,12 @@ def load_library():
     lib.wa_paged_attention.argtypes = [L, p, i32, p, p, p, i32, p, p, i32, f32, i32, p, p, p, sz,
                                        p]
     lib.wa_paged_attention.restype = i32
+    lib.wa_hsa_workspace_bytes.argtypes = [L, i32, i32, i32]
+    lib.wa_hsa_workspace_bytes.restype = sz
+    lib.wa_hsa_select.argtypes = [L, p, i32, p, i32, p, i32, ctypes.c_double, p, p, p, p, p, sz, p]
+    lib.wa_hsa_select.restype = i32
+    lib.wa_sparse_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, p, p, i32, p, p, p]
+    lib.wa_sparse_attention.restype = i32
     lib.wa_status_string.argtypes = [i32]
     lib.wa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -152,6 +159,16 @@ def _need(t, name, dtype=None, min_elems=None, device=True):
     if min_elems is not None and t.numel() < min_elems:
         raise ValueError("%s holds %d elements, the call needs %d" % (name, t.numel(), min_elems))
     return t
+
+
+def _rows(t, name, dt, row):
+    """Token rows of an optional [T][H][d] segment (0 when absent)."""
+    if t is None:
+        return 0
+    _need(t, name, dt)
+    if t.numel() % row:
+        raise ValueError("%s is not a whole number of token rows" % name)
+    return t.numel() // row
 
 
 def _workspace(nbytes, ws, like):
@@ -381,4 +398,89 @@ def wa_paged_attention(L: Layout, q, k_pool, v_pool, idx, k_p, k_own, v_own, sof
                                 float(softmax_scale), int(out_dtype), _ptr(out), _ptr(lse),
                                 _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "wa_paged_attention")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# sparse branch
+
+HSA_CTX_BLOCK, HSA_OWN_BLOCK, HSA_Q_BLOCK = 128, 64, 256
+
+
+def hsa_shape(L: Layout, n_q: int, n_ctx: int, n_own: int):
+    """(q_blocks, items, n_tiles) of a sparse-branch call: the selection
+    writes sel_tiles [items][n_tiles] and sel_count [items], item =
+    head * q_blocks + query block."""
+    q_blocks = -(-int(n_q) // HSA_Q_BLOCK)
+    return q_blocks, q_blocks * L.n_heads, -(-(int(n_ctx) + int(n_own)) // 64)
+
+
+def wa_hsa_workspace_bytes(L: Layout, n_q: int, n_ctx: int, n_own: int) -> int:
+    return int(load_library().wa_hsa_workspace_bytes(ctypes.byref(L), int(n_q), int(n_ctx),
+                                                      int(n_own)))
+
+
+def wa_hsa_select(L: Layout, q, k_ctx, k_own, tau, scale=None, sel_tiles=None, sel_count=None,
+                  gini=None, want_gini=True, workspace=None, stream=None):
+    """Block selection of the sparse branch; returns (sel_tiles [items,
+    n_tiles] int32, sel_count [items] int32, gini [items] float64 or None).
+    tau: device float64 [H]."""
+    lib = load_library()
+    dt, row = L.torch_dtype, L.row_elems
+    _need(q, "q", dt)
+    n_q = q.numel() // row
+    n_ctx, n_own = _rows(k_ctx, "k_ctx", dt, row), _rows(k_own, "k_own", dt, row)
+    _need(tau, "tau", torch.float64, L.n_heads)
+    if scale is None:
+        scale = 1.0 / (L.head_dim ** 0.5)
+    _, items, n_tiles = hsa_shape(L, n_q, n_ctx, n_own)
+    if sel_tiles is None:
+        sel_tiles = torch.empty((items, n_tiles), dtype=torch.int32, device=q.device)
+    if sel_count is None:
+        sel_count = torch.empty(items, dtype=torch.int32, device=q.device)
+    if gini is None and want_gini:
+        gini = torch.empty(items, dtype=torch.float64, device=q.device)
+    _need(sel_tiles, "sel_tiles", torch.int32, items * n_tiles)
+    _need(sel_count, "sel_count", torch.int32, items)
+    if gini is not None:
+        _need(gini, "gini", torch.float64, items)
+    nbytes = lib.wa_hsa_workspace_bytes(ctypes.byref(L), int(n_q), int(n_ctx), int(n_own))
+    ws = _workspace(nbytes, workspace, q)
+    st = lib.wa_hsa_select(ctypes.byref(L), _ptr(q), int(n_q), _ptr(k_ctx), int(n_ctx),
+                           _ptr(k_own), int(n_own), float(scale), _ptr(tau), _ptr(sel_tiles),
+                           _ptr(sel_count), _ptr(gini), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "wa_hsa_select")
+    return sel_tiles, sel_count, gini
+
+
+def wa_sparse_attention(L: Layout, q, k_ctx, v_ctx, k_own, v_own, sel_tiles, sel_count,
+                        softmax_scale=None, out_dtype=None, out=None, lse=None, stream=None):
+    """Attention of each (query block, head) over its listed 64-key tiles of
+    [k_ctx ++ k_own]; returns out [n_q, H, d]."""
+    lib = load_library()
+    dt, row = L.torch_dtype, L.row_elems
+    _need(q, "q", dt)
+    n_q = q.numel() // row
+    n_ctx, n_ctx_v = _rows(k_ctx, "k_ctx", dt, row), _rows(v_ctx, "v_ctx", dt, row)
+    n_own, n_own_v = _rows(k_own, "k_own", dt, row), _rows(v_own, "v_own", dt, row)
+    if n_ctx != n_ctx_v or n_own != n_own_v:
+        raise ValueError("K and V segments differ in length")
+    _, items, n_tiles = hsa_shape(L, n_q, n_ctx, n_own)
+    _need(sel_tiles, "sel_tiles", torch.int32, items * n_tiles)
+    _need(sel_count, "sel_count", torch.int32, items)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / (L.head_dim ** 0.5)
+    if out_dtype is None:
+        out_dtype = L.dtype
+    odt = _TORCH_DTYPE[out_dtype]
+    if out is None:
+        out = torch.empty((n_q, L.n_heads, L.head_dim), dtype=odt, device=q.device)
+    _need(out, "out", odt, n_q * row)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, n_q * L.n_heads)
+    st = lib.wa_sparse_attention(ctypes.byref(L), _ptr(q), int(n_q), _ptr(k_ctx), _ptr(v_ctx),
+                                 int(n_ctx), _ptr(k_own), _ptr(v_own), int(n_own),
+                                 float(softmax_scale), _ptr(sel_tiles), _ptr(sel_count),
+                                 int(out_dtype), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "wa_sparse_attention")
     return out

@@ -102,6 +102,10 @@ struct AttnArgs {
     int max_pages;
     int tpp;            // 64-key tiles per page when page_tokens % 64 == 0, else 0
     uint64_t page_bytes;   // pool page stride in bytes
+    // sparse branch (MODE 3): item i attends over the ascending 64-key tiles
+    // sp_tiles[i * n_tiles + 0 .. sp_count[i]) of [ctx ++ own]
+    const int32_t *sp_tiles;
+    const int32_t *sp_count;
 };
 
 // Work order of a split launch.  Position g in [0, items * T) names one 64-key
@@ -200,6 +204,10 @@ static constexpr unsigned kTileBytes = kTileElems * 2;
 static constexpr int kStageBytes = kTileElems * 2;   // one K or V tile
 static constexpr int kSubBytes = 32 * kD * 2;        // one 32-key sub-tile
 __shared__ __attribute__((aligned(1024))) uint16_t lds_ring[2 * kStages * kTileElems];
+// MODE 3: this block's tile list (only that kernel references it, so only it
+// allocates the 16 KB)
+__shared__ int sp_list[WA_MAX_SPARSE_TILES];
+static_assert(WA_HSA_Q_BLOCK == kBM, "one pooled query block per attention block");
 
 template <int S>
 struct StageTag {
@@ -221,7 +229,9 @@ __device__ __forceinline__ uint16_t *vst() {
 // buffer; MODE 1, pool pages through a.idx, page_tokens a multiple of 64
 // (whole tiles per page: the copies take the same fast path as a contiguous
 // buffer); MODE 2, pool pages, other page sizes (context tiles copied row by
-// row).
+// row); MODE 3, contiguous buffers and a list of tiles per item (the sparse
+// branch): the loop runs over list positions, and each copy looks its tile
+// up in the list.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bf16(AttnArgs a) {
@@ -303,6 +313,12 @@ void k_attn_bf16(AttnArgs a) {
         return av;
     };
 
+    // MODE 3: the tile at list position `pos` (the list is in LDS, the same
+    // for every lane)
+    auto sp_tile = [&](int pos) __attribute__((always_inline)) -> int {
+        return __builtin_amdgcn_readfirstlane(sp_list[pos]);
+    };
+
   // One segment: tiles [t_begin, t_end) of item `item` (query block
   // item % q_blocks of head item / q_blocks).  Without the split a segment is
   // a whole item, normalised and written out; with it, a piece leaves its
@@ -343,8 +359,9 @@ void k_attn_bf16(AttnArgs a) {
     if (MODE == 1 && t_begin < t_ctx) set_page(t_begin / a.tpp);
 
     static_assert(kCopies == 2, "issue_tile writes two 1 KB copies per tensor");
-    auto issue_tile = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    auto issue_tile = [&](int pos, auto stage_tag) __attribute__((always_inline)) {
         constexpr unsigned S = decltype(stage_tag)::value;
+        const int t = MODE == 3 ? sp_tile(pos) : pos;
         constexpr unsigned OK = S * kTileBytes, OV = (kStages + S) * kTileBytes;
         constexpr unsigned ROWS4 = 4 * kD * 2;    // four tile rows
         const int key0 = t * kBN;
@@ -496,10 +513,14 @@ void k_attn_bf16(AttnArgs a) {
     static_assert(2 * kCopies == 4, "the waits below count 4 copies per tile");
     __syncthreads();
     const int t_last = t_end - 1;
-    // the tile whose second half is masked, and the one before it (whose
-    // successor's first half is masked); -2 when the keys fill every tile
-    const int mask_tile = ragged ? n_tiles - 1 : -2;
-    const int mask_tile_prev = ragged ? n_tiles - 2 : -2;
+    // the position of the tile whose second half is masked (the last tile,
+    // keys [mask_key0, n_keys)), and the one before it (whose successor's
+    // first half is masked); -2 when the keys fill every tile or the list
+    // leaves the last tile out
+    int mask_tile = ragged ? n_tiles - 1 : -2;
+    if (MODE == 3) mask_tile = ragged && sp_tile(t_last) == n_tiles - 1 ? t_last : -2;
+    const int mask_tile_prev = mask_tile >= 0 ? mask_tile - 1 : -2;
+    const int mask_key0 = (n_tiles - 1) * kBN;
     issue_tile(t_begin, StageTag<0>{});
     issue_tile(min(t_begin + 1, t_last), StageTag<1>{});
     issue_tile(min(t_begin + 2, t_last), StageTag<2>{});
@@ -517,7 +538,7 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int st = 0; st < 8; ++st)
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sa, 0, 0, 0);
-        if (ragged && t_begin == n_tiles - 1) mask_tail(sa, t_begin * kBN);
+        if (t_begin == mask_tile) mask_tail(sa, mask_key0);
         ak[0] = read_k(kSubBytes, 0);
         ak[1] = read_k(kSubBytes, 1);
     }
@@ -542,10 +563,10 @@ void k_attn_bf16(AttnArgs a) {
         __syncthreads();
         issue_tile(min(t + 3, t_last), StageTag<S3>{});
         pv(KS, pa, av, KS1, ak);
-        if (t == mask_tile) mask_tail(sb, t * kBN + 32);
+        if (t == mask_tile) mask_tail(sb, mask_key0 + 32);
         qk_softmax(KS1, sa, sb, pbk, ak, KS + kSubBytes, av);
         pv(KS + kSubBytes, pbk, av, KS1 + kSubBytes, ak);
-        if (t == mask_tile_prev && !last) mask_tail(sa, (t + 1) * kBN);
+        if (t == mask_tile_prev && !last) mask_tail(sa, mask_key0);
         return last;
     };
     for (int t = t_begin;; t += 4) {
@@ -595,6 +616,20 @@ void k_attn_bf16(AttnArgs a) {
   };
 
     // ---- this block's work: one whole item, or (split) its run of positions
+    if (MODE == 3) {
+        // the item's tile list into LDS (published by the barrier at the top
+        // of the segment); a count or an entry out of range is clamped, so
+        // that every copy stays inside the keys and the loop ends
+        int cnt = __builtin_amdgcn_readfirstlane(a.sp_count[blk]);
+        cnt = cnt < 1 ? 1 : (cnt > n_tiles ? n_tiles : cnt);
+        const int32_t *src = a.sp_tiles + (int64_t)blk * n_tiles;
+        for (int i = tid; i < cnt; i += kThreads) {
+            const int v = src[i];
+            sp_list[i] = v < 0 ? 0 : (v >= n_tiles ? n_tiles - 1 : v);
+        }
+        segment(blk, 0, cnt, 0);
+        return;
+    }
     if (!a.split) {
         segment(blk, 0, n_tiles, 0);
         return;
@@ -722,7 +757,7 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
                                  const uint16_t *k_own, const uint16_t *v_own, int32_t n_own,
                                  float scale, int32_t out_dtype, void *out, float *lse,
                                  const AttnPlan &plan, void *workspace, const PagedCtx &pg,
-                                 hipStream_t s) {
+                                 hipStream_t s, const SparseCtx &sp) {
     AttnArgs a;
     a.q = q;
     a.k_ctx = k_ctx;
@@ -752,6 +787,16 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
     a.max_pages = pg.max_pages;
     a.tpp = pg.idx && pg.page_tokens % kBN == 0 ? pg.page_tokens / kBN : 0;
     a.page_bytes = (uint64_t)pg.page_tokens * (uint64_t)n_heads * kD * 2u;
+    a.sp_tiles = sp.tiles;
+    a.sp_count = sp.count;
+    if (sp.tiles) {
+        // one block per item over its list, never split
+        a.split = 0;
+        a.grid = plan.items;
+        a.part_o = a.part_ml = nullptr;
+        hipLaunchKernelGGL(k_attn_bf16<3>, dim3((unsigned)plan.items), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
     if (!pg.idx)
         hipLaunchKernelGGL(k_attn_bf16<0>, dim3((unsigned)plan.grid), dim3(kThreads), 0, s, a);
     else if (a.tpp > 0)

@@ -163,7 +163,8 @@ namespace {
 wa_status attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
                     const void *v_ctx, int32_t n_ctx, const void *k_own, const void *v_own,
                     int32_t n_own, float softmax_scale, int32_t out_dtype, void *out, float *lse,
-                    void *workspace, size_t ws_bytes, const PagedCtx &pg, void *stream) {
+                    void *workspace, size_t ws_bytes, const PagedCtx &pg, void *stream,
+                    const SparseCtx &sp = SparseCtx{}) {
     if (!q || !out) return WA_ERR_INVALID_ARG;
     if (n_q < 1 || n_ctx < 0 || n_own < 0 || (int64_t)n_ctx + n_own < 1) return WA_ERR_INVALID_ARG;
     if ((int64_t)n_ctx + n_own > 0x7fffffff - 256) return WA_ERR_UNSUPPORTED;
@@ -173,6 +174,10 @@ wa_status attention(const wa_layout *L, const void *q, int32_t n_q, const void *
     if (!aligned16(q) || !aligned16(out) || (n_ctx > 0 && (!aligned16(k_ctx) || !aligned16(v_ctx))) ||
         (n_own > 0 && (!aligned16(k_own) || !aligned16(v_own))) || ((uintptr_t)lse & 3u))
         return WA_ERR_INVALID_ARG;
+    if (sp.tiles) {   // sparse branch: bf16 only, tile lists bounded, never split
+        if (L->dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
+        if (((int64_t)n_ctx + n_own + 63) / 64 > WA_MAX_SPARSE_TILES) return WA_ERR_UNSUPPORTED;
+    }
     if (L->dtype == WA_F32) {
         if (L->head_dim != 64 && L->head_dim != 128) return WA_ERR_UNSUPPORTED;
         if (out_dtype != WA_F32) return WA_ERR_UNSUPPORTED;
@@ -185,13 +190,13 @@ wa_status attention(const wa_layout *L, const void *q, int32_t n_q, const void *
     if (L->head_dim != 128) return WA_ERR_UNSUPPORTED;
     if (out_dtype != WA_F32 && out_dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
     const AttnPlan plan = attention_plan(L->n_heads, n_q, n_ctx + n_own, current_cu_count());
-    if (plan.workspace > 0 && (!workspace || ws_bytes < plan.workspace || !aligned16(workspace)))
+    if (!sp.tiles && plan.workspace > 0 && (!workspace || ws_bytes < plan.workspace || !aligned16(workspace)))
         return WA_ERR_INVALID_ARG;
     return from_hip(launch_attention_bf16(L->n_heads, (const uint16_t *)q, n_q,
                                           (const uint16_t *)k_ctx, (const uint16_t *)v_ctx, n_ctx,
                                           (const uint16_t *)k_own, (const uint16_t *)v_own, n_own,
                                           softmax_scale, out_dtype, out, lse, plan, workspace, pg,
-                                          (hipStream_t)stream));
+                                          (hipStream_t)stream, sp));
 }
 
 }  // namespace
@@ -224,6 +229,56 @@ wa_status wa_paged_attention(const wa_layout *L, const void *q, int32_t n_q, con
     pg.max_pages = L->max_pages;
     return attention(L, q, n_q, k_pool, v_pool, k_p * L->page_tokens, k_own, v_own, n_own,
                      softmax_scale, out_dtype, out, lse, workspace, ws_bytes, pg, stream);
+}
+
+size_t wa_hsa_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_ctx, int32_t n_own) {
+    if (check_layout(L, false) != WA_OK) return 0;
+    if (n_q < 1 || n_ctx < 0 || n_own < 0 || (int64_t)n_ctx + n_own < 1) return 0;
+    if (n_ctx % 64 != 0 || L->head_dim > WA_HSA_MAX_HEAD_DIM) return 0;
+    const HsaShape w = hsa_shape(L->n_heads, n_q, n_ctx, n_own);
+    if (w.nb_ctx + w.nb_own > WA_MAX_HSA_BLOCKS) return 0;
+    if ((int64_t)w.nb_ctx + w.nb_own + w.q_blocks > 65535) return 0;
+    return hsa_workspace_bytes((int64_t)L->n_heads * L->head_dim, w);
+}
+
+wa_status wa_hsa_select(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
+                        int32_t n_ctx, const void *k_own, int32_t n_own, double scale,
+                        const double *tau, int32_t *sel_tiles, int32_t *sel_count, double *gini,
+                        void *workspace, size_t ws_bytes, void *stream) {
+    const wa_status st = check_layout(L, false);
+    if (st != WA_OK) return st;
+    if (!q || !tau || !sel_tiles || !sel_count || !workspace) return WA_ERR_INVALID_ARG;
+    if (n_q < 1 || n_ctx < 0 || n_own < 0 || (int64_t)n_ctx + n_own < 1) return WA_ERR_INVALID_ARG;
+    if ((n_ctx > 0 && !k_ctx) || (n_own > 0 && !k_own)) return WA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.0)) return WA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(workspace) || (n_ctx > 0 && !aligned16(k_ctx)) ||
+        (n_own > 0 && !aligned16(k_own)) || ((uintptr_t)tau & 7u) || ((uintptr_t)gini & 7u) ||
+        ((uintptr_t)sel_tiles & 3u) || ((uintptr_t)sel_count & 3u))
+        return WA_ERR_INVALID_ARG;
+    if (n_ctx % 64 != 0 || L->head_dim > WA_HSA_MAX_HEAD_DIM) return WA_ERR_UNSUPPORTED;
+    const HsaShape w = hsa_shape(L->n_heads, n_q, n_ctx, n_own);
+    if (w.nb_ctx + w.nb_own > WA_MAX_HSA_BLOCKS) return WA_ERR_UNSUPPORTED;
+    if ((int64_t)w.nb_ctx + w.nb_own + w.q_blocks > 65535) return WA_ERR_UNSUPPORTED;
+    if (ws_bytes < hsa_workspace_bytes((int64_t)L->n_heads * L->head_dim, w))
+        return WA_ERR_INVALID_ARG;
+    return from_hip(launch_hsa_select(*L, q, n_q, k_ctx, n_ctx, k_own, n_own, scale, tau,
+                                      sel_tiles, sel_count, gini, workspace, (hipStream_t)stream));
+}
+
+wa_status wa_sparse_attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
+                              const void *v_ctx, int32_t n_ctx, const void *k_own,
+                              const void *v_own, int32_t n_own, float softmax_scale,
+                              const int32_t *sel_tiles, const int32_t *sel_count,
+                              int32_t out_dtype, void *out, float *lse, void *stream) {
+    const wa_status st = check_layout(L, false);
+    if (st != WA_OK) return st;
+    if (!sel_tiles || !sel_count) return WA_ERR_INVALID_ARG;
+    if (((uintptr_t)sel_tiles & 3u) || ((uintptr_t)sel_count & 3u)) return WA_ERR_INVALID_ARG;
+    SparseCtx sp;
+    sp.tiles = sel_tiles;
+    sp.count = sel_count;
+    return attention(L, q, n_q, k_ctx, v_ctx, n_ctx, k_own, v_own, n_own, softmax_scale,
+                     out_dtype, out, lse, nullptr, 0, PagedCtx{}, stream, sp);
 }
 
 const char *wa_status_string(wa_status s) {

@@ -103,11 +103,38 @@ struct AttnPlan {
 };
 AttnPlan attention_plan(int32_t n_heads, int32_t n_q, int32_t n_keys, int cu_count);
 
+// Sparse branch: per (query block, head) item, the ascending 64-key tiles of
+// [ctx ++ own] to attend over (tiles[item][0 .. count[item])).  tiles == null:
+// every tile (dense attention).
+struct SparseCtx {
+    const int32_t *tiles = nullptr;   // device [items][n_tiles]
+    const int32_t *count = nullptr;   // device [items]
+};
+
 hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q,
                                  const uint16_t *k_ctx, const uint16_t *v_ctx, int32_t n_ctx,
                                  const uint16_t *k_own, const uint16_t *v_own, int32_t n_own,
                                  float scale, int32_t out_dtype, void *out, float *lse,
                                  const AttnPlan &plan, void *workspace, const PagedCtx &pg,
-                                 hipStream_t s);
+                                 hipStream_t s, const SparseCtx &sp = SparseCtx{});
+
+// ---------------------------------------------------------------------------
+// sparse branch block selection
+
+struct HsaShape {
+    int32_t nb_ctx;     // context key blocks
+    int32_t nb_own;     // own key blocks
+    int32_t q_blocks;   // pooled query blocks
+    int32_t items;      // q_blocks * n_heads, item = head * q_blocks + query block
+    int32_t n_tiles;    // 64-key tiles of [ctx ++ own] (row stride of the tile lists)
+};
+HsaShape hsa_shape(int32_t n_heads, int32_t n_q, int32_t n_ctx, int32_t n_own);
+// key block sums [nb_ctx + nb_own][hd], then query block sums [q_blocks][hd] (fp64)
+size_t hsa_workspace_bytes(int64_t hd, const HsaShape &w);
+
+hipError_t launch_hsa_select(const wa_layout &L, const void *q, int32_t n_q, const void *k_ctx,
+                             int32_t n_ctx, const void *k_own, int32_t n_own, double scale,
+                             const double *tau, int32_t *tiles, int32_t *count, double *gini,
+                             void *ws, hipStream_t s);
 
 }  // namespace wa

@@ -297,3 +297,86 @@ def test_paged_attention_rejects(lib):
     assert lib.wa_attention_workspace_bytes(L(), 1024, 2 * 12480, 300) > 0
     assert _pattn(lib, **big) == E                           # workspace missing
     assert _pattn(lib, ws=A, ws_bytes=1024, **big) == E      # too small
+
+
+# ---------------------------------------------------------------------------
+# sparse branch (every case below is rejected on the host: nothing launches)
+
+def test_hsa_workspace_size(lib):
+    """fp64 key-block sums [390 context + 74 own blocks][1536] (256-byte
+    aligned), then query-block sums [19][1536], for 49,920 + 4,680 keys and
+    4,680 queries of 12 x 128."""
+    kb = (390 + 74) * 1536 * 8
+    assert lib.wa_hsa_workspace_bytes(L(), 4680, 49920, 4680) == \
+        (kb + 255) // 256 * 256 + 19 * 1536 * 8
+    assert lib.wa_hsa_workspace_bytes(L(), 4680, 49900, 4680) == 0      # n_ctx % 64
+    assert lib.wa_hsa_workspace_bytes(L(), 0, 64, 64) == 0
+    assert lib.wa_hsa_workspace_bytes(L(), 64, 0, 0) == 0
+    assert lib.wa_hsa_workspace_bytes(L(), 64, 128 * 2048, 64) == 0     # 2,049 key blocks
+    assert lib.wa_hsa_workspace_bytes(L(H=2, d=512), 64, 64, 64) == 0   # head_dim > 256
+    assert lib.wa_hsa_workspace_bytes(None, 64, 64, 64) == 0
+
+
+def _hsel(lib, lay=None, q=A, n_q=300, kc=A, n_ctx=640, ko=B, n_own=100, scale=0.1, tau=A,
+          tiles=B, count=A, gini=NULL, ws=A, ws_bytes=1 << 20):
+    return lib.wa_hsa_select(lay if lay is not None else L(), q, n_q, kc, n_ctx, ko, n_own, scale,
+                             tau, tiles, count, gini, ws, ws_bytes, None)
+
+
+def test_hsa_select_rejects(lib):
+    """Every argument rule of wa_hsa_select, one bad argument per call."""
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert lib.wa_hsa_select(None, A, 300, A, 640, B, 100, 0.1, A, B, A, NULL, A, 1 << 20,
+                             None) == E
+    for bad in ("q", "tau", "tiles", "count", "ws"):
+        assert _hsel(lib, **{bad: NULL}) == E, bad
+    assert _hsel(lib, n_q=0) == E
+    assert _hsel(lib, n_ctx=-64) == E
+    assert _hsel(lib, n_own=-1) == E
+    assert _hsel(lib, n_ctx=0, n_own=0) == E
+    assert _hsel(lib, kc=NULL) == E
+    assert _hsel(lib, ko=NULL) == E
+    for s in (float("nan"), float("inf"), 0.0, -1.0):
+        assert _hsel(lib, scale=s) == E
+    assert _hsel(lib, q=MIS) == E
+    assert _hsel(lib, ws=MIS) == E
+    assert _hsel(lib, kc=MIS) == E
+    assert _hsel(lib, tau=ctypes.c_void_p(0x10004)) == E     # double alignment
+    assert _hsel(lib, gini=ctypes.c_void_p(0x10004)) == E
+    assert _hsel(lib, tiles=ctypes.c_void_p(0x10002)) == E   # int32 alignment
+    assert _hsel(lib, count=ctypes.c_void_p(0x10002)) == E
+    assert _hsel(lib, ws_bytes=1024) == E                    # workspace too small
+    assert _hsel(lib, n_ctx=100) == U                        # context not whole tiles
+    assert _hsel(lib, lay=L(H=2, d=512)) == U                # head_dim > 256
+    assert _hsel(lib, n_ctx=128 * 2048, n_own=64) == U       # 2,049 key blocks
+    assert _hsel(lib, lay=L(dtype=7)) == U
+
+
+def _sattn(lib, lay=None, q=A, n_q=64, kc=A, vc=B, n_ctx=64, ko=A, vo=B, n_own=64, scale=0.1,
+           tiles=A, count=B, odt=wa.WA_F32, out=B, lse=NULL):
+    return lib.wa_sparse_attention(lay if lay is not None else L(), q, n_q, kc, vc, n_ctx, ko, vo,
+                                   n_own, scale, tiles, count, odt, out, lse, None)
+
+
+def test_sparse_attention_rejects(lib):
+    """Every argument rule of wa_sparse_attention, one bad argument per call."""
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert lib.wa_sparse_attention(None, A, 64, A, B, 64, A, B, 64, 0.1, A, B, wa.WA_F32, B, NULL,
+                                   None) == E
+    assert _sattn(lib, tiles=NULL) == E
+    assert _sattn(lib, count=NULL) == E
+    assert _sattn(lib, tiles=ctypes.c_void_p(0x10002)) == E
+    assert _sattn(lib, count=ctypes.c_void_p(0x10002)) == E
+    assert _sattn(lib, q=NULL) == E
+    assert _sattn(lib, out=NULL) == E
+    assert _sattn(lib, n_q=0) == E
+    assert _sattn(lib, n_ctx=-1) == E
+    assert _sattn(lib, n_ctx=0, n_own=0) == E
+    assert _sattn(lib, kc=NULL) == E
+    assert _sattn(lib, vo=NULL) == E
+    assert _sattn(lib, scale=float("nan")) == E
+    assert _sattn(lib, q=MIS) == E
+    assert _sattn(lib, lay=L(dtype=wa.WA_F32)) == U           # bf16 only
+    assert _sattn(lib, lay=L(d=64)) == U                      # head_dim 128
+    assert _sattn(lib, odt=5) == U
+    assert _sattn(lib, n_ctx=64 * 4096, n_own=64) == U        # 4,097 tiles

@@ -24,7 +24,12 @@ Value recipe (the pages fix none; stated so both sides can reproduce it):
   and ``c_j = 0.5 * (1 + pi(j))`` for a seeded permutation ``pi`` over every
   page the workload ever holds.  Offsets are therefore 0.5 apart and their
   order differs from page order, so page scores do not tie.  Values carry no
-  offset.
+  offset;
+* for the sparse branch, ``aligned_queries`` shifts the chunk's queries by
+  ``gain * u`` (the same noise as ``chunk_qkv``'s queries): the pooled
+  attention map then favours the blocks of the pages with large ``c_j``, as a
+  head that attends to a few places would, instead of the near-uniform map
+  that i.i.d. queries give.
 """
 from __future__ import annotations
 
@@ -206,6 +211,12 @@ def chunk_qkv(wl: Workload, chunk: int, step: int) -> tuple[np.ndarray, np.ndarr
     k = _draw_rows(wl, TAG_KOWN, chunk, step, wl.n_q)
     v = _draw_rows(wl, TAG_VOWN, chunk, step, wl.n_q)
     return q, k, v
+
+
+def aligned_queries(wl: Workload, chunk: int, step: int, gain: float) -> np.ndarray:
+    """The queries of ``chunk_qkv`` shifted by ``gain * u`` before rounding."""
+    shift = (np.float32(gain) * offset_direction(wl)).astype(np.float32)
+    return _draw_rows(wl, TAG_Q, chunk, step, wl.n_q, shift)
 
 
 def chunk_prompts(wl: Workload) -> np.ndarray:
