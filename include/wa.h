@@ -358,17 +358,31 @@ wa_status wa_hsa_select(const wa_layout *layout, const void *q, int32_t n_q, con
  * (a count or an entry outside its range is clamped so that every access
  * stays inside the keys, and the result is then unspecified).  Other
  * arguments as wa_block_attention; layout.dtype must be WA_BF16 and head_dim
- * 128.  No workspace: every (query block, head) runs in one workgroup.
+ * 128.  The counts stay on the device: a first kernel lays the lists end to
+ * end and, when they are uneven enough that one workgroup per item would
+ * leave CUs idle, the lists are cut into equal runs over all CUs and the
+ * pieces merged (otherwise the result is bit for bit that of
+ * wa_block_attention over the same tiles laid end to end).
+ * workspace: device, >= wa_sparse_workspace_bytes bytes, 16-byte aligned,
+ * not shared by calls in flight at once.
  * Errors: as wa_block_attention, plus NULL or misaligned sel_tiles /
- * sel_count -> WA_ERR_INVALID_ARG; a WA_F32 layout, more than
- * WA_MAX_SPARSE_TILES tiles -> WA_ERR_UNSUPPORTED.
+ * sel_count, workspace missing or too small -> WA_ERR_INVALID_ARG; a WA_F32
+ * layout, more than WA_MAX_SPARSE_TILES tiles, more than 2^31 - 1 list
+ * entries in all -> WA_ERR_UNSUPPORTED.
  */
 wa_status wa_sparse_attention(const wa_layout *layout, const void *q, int32_t n_q,
                               const void *k_ctx, const void *v_ctx, int32_t n_ctx,
                               const void *k_own, const void *v_own, int32_t n_own,
                               float softmax_scale, const int32_t *sel_tiles,
                               const int32_t *sel_count, int32_t out_dtype, void *out,
-                              float *lse, void *stream);
+                              float *lse, void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace wa_sparse_attention needs for these arguments on the
+ * current device (0 for arguments it would reject): the launch plan, the
+ * running list offsets and partial results of (query blocks x heads + CUs)
+ * pieces.  Launches nothing. */
+size_t wa_sparse_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ctx,
+                                 int32_t n_own);
 
 /* Static text describing a status code. */
 const char *wa_status_string(wa_status status);

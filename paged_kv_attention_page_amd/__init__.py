@@ -25,7 +25,8 @@ __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "W
            "wa_append_workspace_bytes", "wa_append_page", "wa_select_workspace_bytes",
            "wa_select_pages", "wa_select_window", "wa_gather", "wa_attention_workspace_bytes",
            "wa_block_attention", "wa_paged_attention", "hsa_shape", "wa_hsa_workspace_bytes",
-           "wa_hsa_select", "wa_sparse_attention", "wa_status_string"]
+           "wa_hsa_select", "wa_sparse_workspace_bytes", "wa_sparse_attention",
+           "wa_status_string"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -110,7 +111,10 @@ def load_library():
     lib.wa_hsa_workspace_bytes.restype = sz
     lib.wa_hsa_select.argtypes = [L, p, i32, p, i32, p, i32, ctypes.c_double, p, p, p, p, p, sz, p]
     lib.wa_hsa_select.restype = i32
-    lib.wa_sparse_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, p, p, i32, p, p, p]
+    lib.wa_sparse_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, p, p, i32, p, p, p,
+                                        sz, p]
+    lib.wa_sparse_workspace_bytes.argtypes = [L, i32, i32, i32]
+    lib.wa_sparse_workspace_bytes.restype = sz
     lib.wa_sparse_attention.restype = i32
     lib.wa_status_string.argtypes = [i32]
     lib.wa_status_string.restype = ctypes.c_char_p
@@ -453,8 +457,14 @@ def wa_hsa_select(L: Layout, q, k_ctx, k_own, tau, scale=None, sel_tiles=None, s
     return sel_tiles, sel_count, gini
 
 
+def wa_sparse_workspace_bytes(L: Layout, n_q: int, n_ctx: int, n_own: int) -> int:
+    return int(load_library().wa_sparse_workspace_bytes(ctypes.byref(L), int(n_q), int(n_ctx),
+                                                         int(n_own)))
+
+
 def wa_sparse_attention(L: Layout, q, k_ctx, v_ctx, k_own, v_own, sel_tiles, sel_count,
-                        softmax_scale=None, out_dtype=None, out=None, lse=None, stream=None):
+                        softmax_scale=None, out_dtype=None, out=None, lse=None, workspace=None,
+                        stream=None):
     """Attention of each (query block, head) over its listed 64-key tiles of
     [k_ctx ++ k_own]; returns out [n_q, H, d]."""
     lib = load_library()
@@ -478,9 +488,12 @@ def wa_sparse_attention(L: Layout, q, k_ctx, v_ctx, k_own, v_own, sel_tiles, sel
     _need(out, "out", odt, n_q * row)
     if lse is not None:
         _need(lse, "lse", torch.float32, n_q * L.n_heads)
+    nbytes = lib.wa_sparse_workspace_bytes(ctypes.byref(L), int(n_q), int(n_ctx), int(n_own))
+    ws = _workspace(nbytes, workspace, q)
     st = lib.wa_sparse_attention(ctypes.byref(L), _ptr(q), int(n_q), _ptr(k_ctx), _ptr(v_ctx),
                                  int(n_ctx), _ptr(k_own), _ptr(v_own), int(n_own),
                                  float(softmax_scale), _ptr(sel_tiles), _ptr(sel_count),
-                                 int(out_dtype), _ptr(out), _ptr(lse), _stream(stream))
+                                 int(out_dtype), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                 _stream(stream))
     _check(st, "wa_sparse_attention")
     return out

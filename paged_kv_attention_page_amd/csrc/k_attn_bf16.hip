@@ -103,9 +103,12 @@ struct AttnArgs {
     int tpp;            // 64-key tiles per page when page_tokens % 64 == 0, else 0
     uint64_t page_bytes;   // pool page stride in bytes
     // sparse branch (MODE 3): item i attends over the ascending 64-key tiles
-    // sp_tiles[i * n_tiles + 0 .. sp_count[i]) of [ctx ++ own]
+    // sp_tiles[i * n_tiles + 0 .. sp_count[i]) of [ctx ++ own]; sp_plan and
+    // sp_prefix are written by k_sparse_plan (see there)
     const int32_t *sp_tiles;
     const int32_t *sp_count;
+    const int32_t *sp_plan;     // [split, blocks taking runs, total positions]
+    const int32_t *sp_prefix;   // [items + 1] exclusive prefix of the (clamped) counts
 };
 
 // Work order of a split launch.  Position g in [0, items * T) names one 64-key
@@ -578,9 +581,11 @@ void k_attn_bf16(AttnArgs a) {
 
     // ---- epilogue: O^T[dv][q] / l; lanes l and l^32 hold halves of l
     const float lt = xhalf_sum(l);
-    if (a.split) {
+    // MODE 3: slot < 0 marks a piece that is a whole item (written out here)
+    if (MODE == 3 ? slot >= 0 : a.split != 0) {
         // piece of an item: unnormalised output, reference max, row sum
-        const int64_t prow = ((int64_t)item * a.slots + slot) * kBM + wave * kWQ + lr;
+        const int64_t prow =
+            (MODE == 3 ? (int64_t)slot : (int64_t)item * a.slots + slot) * kBM + wave * kWQ + lr;
         float *po = a.part_o + prow * kD;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -617,17 +622,49 @@ void k_attn_bf16(AttnArgs a) {
 
     // ---- this block's work: one whole item, or (split) its run of positions
     if (MODE == 3) {
-        // the item's tile list into LDS (published by the barrier at the top
-        // of the segment); a count or an entry out of range is clamped, so
-        // that every copy stays inside the keys and the loop ends
-        int cnt = __builtin_amdgcn_readfirstlane(a.sp_count[blk]);
-        cnt = cnt < 1 ? 1 : (cnt > n_tiles ? n_tiles : cnt);
-        const int32_t *src = a.sp_tiles + (int64_t)blk * n_tiles;
-        for (int i = tid; i < cnt; i += kThreads) {
-            const int v = src[i];
-            sp_list[i] = v < 0 ? 0 : (v >= n_tiles ? n_tiles - 1 : v);
+        // Entries [b, e) of item i's tile list into LDS (published by the
+        // barrier at the top of the segment); an entry out of range is
+        // clamped, so that every copy stays inside the keys.
+        auto load_list = [&](int i, int b, int e) __attribute__((always_inline)) {
+            const int32_t *src = a.sp_tiles + (int64_t)i * n_tiles + b;
+            for (int k = tid; k < e - b; k += kThreads) {
+                const int v = src[k];
+                sp_list[k] = v < 0 ? 0 : (v >= n_tiles ? n_tiles - 1 : v);
+            }
+        };
+        if (__builtin_amdgcn_readfirstlane(a.sp_plan[0]) == 0) {
+            // one block per item (counts clamped into [1, n_tiles] as the
+            // plan does, so that the loop ends)
+            if (blk >= a.items) return;
+            int cnt = __builtin_amdgcn_readfirstlane(a.sp_count[blk]);
+            cnt = cnt < 1 ? 1 : (cnt > n_tiles ? n_tiles : cnt);
+            load_list(blk, 0, cnt);
+            segment(blk, 0, cnt, -1);
+            return;
         }
-        segment(blk, 0, cnt, 0);
+        // split: block blk takes list positions [blk total / G, (blk+1) total
+        // / G) of the items' lists laid end to end; a piece that is not a
+        // whole item leaves a partial result in slot item + blk (pieces in
+        // position order raise item, block or both, so the slots differ)
+        const int geff = __builtin_amdgcn_readfirstlane(a.sp_plan[1]);
+        const int total = __builtin_amdgcn_readfirstlane(a.sp_plan[2]);
+        if (blk >= geff) return;
+        const int g1 = (int)((int64_t)(blk + 1) * total / geff);
+        for (int g = (int)((int64_t)blk * total / geff); g < g1;) {
+            int lo = 0, hi = a.items;   // sp_prefix[lo] <= g < sp_prefix[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (__builtin_amdgcn_readfirstlane(a.sp_prefix[mid]) <= g) lo = mid;
+                else hi = mid;
+            }
+            const int p0 = __builtin_amdgcn_readfirstlane(a.sp_prefix[lo]);
+            const int p1 = __builtin_amdgcn_readfirstlane(a.sp_prefix[lo + 1]);
+            const int e = p1 < g1 ? p1 : g1;
+            __syncthreads();   // every wave is done with the previous piece's list
+            load_list(lo, g - p0, e - p0);
+            segment(lo, 0, e - g, (g == p0 && e == p1) ? -1 : lo + blk);
+            g = e;
+        }
         return;
     }
     if (!a.split) {
@@ -664,12 +701,26 @@ void k_attn_bf16(AttnArgs a) {
 // 256 threads per 8 query rows of an item: lane group (wave, lane / 32) owns
 // a row, 32 lanes x 4 dims cover its 128 dims.
 static constexpr int kMergeRows = 8;
+template <bool SPARSE>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     __shared__ int slot_list[kMaxSlots];
     __shared__ int n_pieces;
     const int item = blockIdx.x / (kBM / kMergeRows);
     const int r = (blockIdx.x % (kBM / kMergeRows)) * kMergeRows + (threadIdx.x >> 5);
-    if (threadIdx.x == 0) {
+    // sparse branch: the pieces of item i are the blocks w0 .. w1 whose runs
+    // meet its positions [P_i, P_i+1), in slots i + w0 .. i + w1; one piece
+    // was written out directly
+    int first_slot = 0, np_sparse = 0;
+    if (SPARSE) {
+        if (a.sp_plan[0] == 0) return;
+        const int64_t geff = a.sp_plan[1], total = a.sp_plan[2];
+        const int64_t p0 = a.sp_prefix[item], p1 = a.sp_prefix[item + 1];
+        const int w0 = (int)(((p0 + 1) * geff - 1) / total);
+        const int w1 = (int)((p1 * geff - 1) / total);
+        if (w0 == w1) return;
+        first_slot = item + w0;
+        np_sparse = w1 - w0 + 1;
+    } else if (threadIdx.x == 0) {
         const SplitMap map(a);
         int n = 0;
         for (int p = 0; p < 2; ++p) {
@@ -681,18 +732,18 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         n_pieces = n;
     }
     __syncthreads();
-    const int np = n_pieces;
+    const int np = SPARSE ? np_sparse : n_pieces;
     const int h = item / a.q_blocks, qb = item % a.q_blocks;
     const int row = qb * kBM + r;
     if (row >= a.n_q) return;
     const int64_t hd = (int64_t)a.n_heads * kD;
     const float c = a.c;
     const int d = 4 * (threadIdx.x & 31);
-    const int64_t row0 = (int64_t)item * a.slots * kBM + r;
+    const int64_t row0 = SPARSE ? (int64_t)first_slot * kBM + r : (int64_t)item * a.slots * kBM + r;
     float M = -INFINITY, L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < np; ++j) {
-        const int64_t pr = row0 + (int64_t)slot_list[j] * kBM;
+        const int64_t pr = row0 + (int64_t)(SPARSE ? j : slot_list[j]) * kBM;
         const float2 ml = *(const float2 *)(a.part_ml + 2 * pr);
         const float4 v = *(const float4 *)(a.part_o + pr * kD + d);
         const float mn = fmaxf(M, ml.x);
@@ -718,6 +769,67 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     }
     if (a.lse && d == 0)
         a.lse[(int64_t)h * a.n_q + row] = (M * c + __log2f(L)) * 0.69314718055994531f;
+}
+
+// Plan of a sparse launch, from the item counts on the device (the host never
+// sees them): the exclusive prefix P of the counts, each clamped into
+// [1, n_tiles] as the attention kernel clamps them, and whether to split.
+// Without the split one block runs each item, so the launch lasts about the
+// longest item times the rounds of blocks (ceil(items / CUs)); with it, G =
+// min(CUs, 32 items) blocks take equal runs of total / G positions.  Split
+// when runs are at least kMinSplitTiles long and the unsplit launch would
+// take over 1.25 times a run (the dense launch measured no faster split at
+// 1.12).  One block of 1024 threads.
+static constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void k_sparse_plan(const int32_t *__restrict__ count,
+                                                              int items, int n_tiles, int cu_count,
+                                                              int32_t *__restrict__ plan,
+                                                              int32_t *__restrict__ prefix) {
+    __shared__ int sc[kPlanThreads];
+    __shared__ int mx[kPlanThreads];
+    const int t = threadIdx.x;
+    const int per = (items + kPlanThreads - 1) / kPlanThreads;
+    const int i0 = min(items, t * per), i1 = min(items, i0 + per);
+    auto clamped = [&](int i) { const int c = count[i]; return c < 1 ? 1 : (c > n_tiles ? n_tiles : c); };
+    int s = 0, m = 0;
+    for (int i = i0; i < i1; ++i) {
+        const int c = clamped(i);
+        s += c;
+        m = max(m, c);
+    }
+    sc[t] = s;
+    mx[t] = m;
+    __syncthreads();
+    for (int d = 1; d < kPlanThreads; d <<= 1) {   // inclusive prefix sum, prefix max
+        const int as = t >= d ? sc[t - d] : 0, am = t >= d ? mx[t - d] : 0;
+        __syncthreads();
+        sc[t] += as;
+        mx[t] = max(mx[t], am);
+        __syncthreads();
+    }
+    int run = sc[t] - s;
+    for (int i = i0; i < i1; ++i) {
+        prefix[i] = run;
+        run += clamped(i);
+    }
+    if (t == kPlanThreads - 1) {
+        const int total = sc[t], maxc = mx[t];
+        prefix[items] = total;
+        const int geff = min(cu_count, items * kMaxBlocksPerItem);
+        const int64_t rounds = (items + cu_count - 1) / cu_count;
+        const int64_t runlen = total / geff;
+        plan[0] = runlen >= kMinSplitTiles && (int64_t)maxc * rounds * 4 > runlen * 5;
+        plan[1] = geff;
+        plan[2] = total;
+    }
+}
+
+// Sparse workspace: plan (256 bytes), prefix [items + 1], then partial
+// outputs and (max, sum) pairs for items + cu_count slots.
+static size_t sparse_prefix_bytes(int items) { return align_up((size_t)(items + 1) * 4, 256); }
+size_t sparse_workspace_bytes(int items, int cu_count) {
+    return 256 + sparse_prefix_bytes(items) +
+           (size_t)(items + cu_count) * kBM * (kD + 2) * sizeof(float);
 }
 
 AttnPlan attention_plan(int32_t n_heads, int32_t n_q, int32_t n_keys, int cu_count) {
@@ -789,12 +901,29 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
     a.page_bytes = (uint64_t)pg.page_tokens * (uint64_t)n_heads * kD * 2u;
     a.sp_tiles = sp.tiles;
     a.sp_count = sp.count;
+    a.sp_plan = a.sp_prefix = nullptr;
     if (sp.tiles) {
-        // one block per item over its list, never split
+        // plan on the device, then one block per item or per CU, then the
+        // merge of split items
+        char *ws = (char *)workspace;
+        int32_t *plan_d = (int32_t *)ws, *prefix = (int32_t *)(ws + 256);
+        a.sp_plan = plan_d;
+        a.sp_prefix = prefix;
         a.split = 0;
-        a.grid = plan.items;
-        a.part_o = a.part_ml = nullptr;
-        hipLaunchKernelGGL(k_attn_bf16<3>, dim3((unsigned)plan.items), dim3(kThreads), 0, s, a);
+        a.slots = 0;
+        a.grid = sp.cu_count;
+        a.part_o = (float *)(ws + 256 + sparse_prefix_bytes(plan.items));
+        a.part_ml = a.part_o + (size_t)(plan.items + sp.cu_count) * kBM * kD;
+        hipLaunchKernelGGL(k_sparse_plan, dim3(1), dim3(kPlanThreads), 0, s, sp.count, plan.items,
+                           plan.n_tiles, sp.cu_count, plan_d, prefix);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int grid = plan.items > sp.cu_count ? plan.items : sp.cu_count;
+        hipLaunchKernelGGL(k_attn_bf16<3>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_attn_merge<true>, dim3((unsigned)(plan.items * (kBM / kMergeRows))),
+                           dim3(256), 0, s, a);
         return hipGetLastError();
     }
     if (!pg.idx)
@@ -805,7 +934,7 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
         hipLaunchKernelGGL(k_attn_bf16<2>, dim3((unsigned)plan.grid), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !plan.split) return e;
-    hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(a.q_blocks * n_heads * (kBM / kMergeRows))),
+    hipLaunchKernelGGL(k_attn_merge<false>, dim3((unsigned)(a.q_blocks * n_heads * (kBM / kMergeRows))),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }

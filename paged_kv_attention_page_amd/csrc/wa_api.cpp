@@ -174,9 +174,11 @@ wa_status attention(const wa_layout *L, const void *q, int32_t n_q, const void *
     if (!aligned16(q) || !aligned16(out) || (n_ctx > 0 && (!aligned16(k_ctx) || !aligned16(v_ctx))) ||
         (n_own > 0 && (!aligned16(k_own) || !aligned16(v_own))) || ((uintptr_t)lse & 3u))
         return WA_ERR_INVALID_ARG;
-    if (sp.tiles) {   // sparse branch: bf16 only, tile lists bounded, never split
+    if (sp.tiles) {   // sparse branch: bf16 only, tile lists bounded
         if (L->dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
-        if (((int64_t)n_ctx + n_own + 63) / 64 > WA_MAX_SPARSE_TILES) return WA_ERR_UNSUPPORTED;
+        const int64_t n_tiles = ((int64_t)n_ctx + n_own + 63) / 64;
+        if (n_tiles > WA_MAX_SPARSE_TILES) return WA_ERR_UNSUPPORTED;
+        if ((int64_t)(n_q + 255) / 256 * L->n_heads * n_tiles > 0x7fffffff) return WA_ERR_UNSUPPORTED;
     }
     if (L->dtype == WA_F32) {
         if (L->head_dim != 64 && L->head_dim != 128) return WA_ERR_UNSUPPORTED;
@@ -190,7 +192,11 @@ wa_status attention(const wa_layout *L, const void *q, int32_t n_q, const void *
     if (L->head_dim != 128) return WA_ERR_UNSUPPORTED;
     if (out_dtype != WA_F32 && out_dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
     const AttnPlan plan = attention_plan(L->n_heads, n_q, n_ctx + n_own, current_cu_count());
-    if (!sp.tiles && plan.workspace > 0 && (!workspace || ws_bytes < plan.workspace || !aligned16(workspace)))
+    if (sp.tiles) {
+        if (!workspace || !aligned16(workspace) ||
+            ws_bytes < sparse_workspace_bytes(plan.items, sp.cu_count))
+            return WA_ERR_INVALID_ARG;
+    } else if (plan.workspace > 0 && (!workspace || ws_bytes < plan.workspace || !aligned16(workspace)))
         return WA_ERR_INVALID_ARG;
     return from_hip(launch_attention_bf16(L->n_heads, (const uint16_t *)q, n_q,
                                           (const uint16_t *)k_ctx, (const uint16_t *)v_ctx, n_ctx,
@@ -265,11 +271,23 @@ wa_status wa_hsa_select(const wa_layout *L, const void *q, int32_t n_q, const vo
                                       sel_tiles, sel_count, gini, workspace, (hipStream_t)stream));
 }
 
+size_t wa_sparse_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_ctx,
+                                 int32_t n_own) {
+    if (check_layout(L, false) != WA_OK || L->dtype != WA_BF16) return 0;
+    if (n_q < 1 || n_ctx < 0 || n_own < 0 || (int64_t)n_ctx + n_own < 1) return 0;
+    const int64_t n_tiles = ((int64_t)n_ctx + n_own + 63) / 64;
+    if (n_tiles > WA_MAX_SPARSE_TILES) return 0;
+    const int64_t items = (int64_t)(n_q + 255) / 256 * L->n_heads;
+    if (items * n_tiles > 0x7fffffff) return 0;
+    return sparse_workspace_bytes((int)items, current_cu_count());
+}
+
 wa_status wa_sparse_attention(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
                               const void *v_ctx, int32_t n_ctx, const void *k_own,
                               const void *v_own, int32_t n_own, float softmax_scale,
                               const int32_t *sel_tiles, const int32_t *sel_count,
-                              int32_t out_dtype, void *out, float *lse, void *stream) {
+                              int32_t out_dtype, void *out, float *lse, void *workspace,
+                              size_t ws_bytes, void *stream) {
     const wa_status st = check_layout(L, false);
     if (st != WA_OK) return st;
     if (!sel_tiles || !sel_count) return WA_ERR_INVALID_ARG;
@@ -277,8 +295,9 @@ wa_status wa_sparse_attention(const wa_layout *L, const void *q, int32_t n_q, co
     SparseCtx sp;
     sp.tiles = sel_tiles;
     sp.count = sel_count;
+    sp.cu_count = current_cu_count();
     return attention(L, q, n_q, k_ctx, v_ctx, n_ctx, k_own, v_own, n_own, softmax_scale,
-                     out_dtype, out, lse, nullptr, 0, PagedCtx{}, stream, sp);
+                     out_dtype, out, lse, workspace, ws_bytes, PagedCtx{}, stream, sp);
 }
 
 const char *wa_status_string(wa_status s) {

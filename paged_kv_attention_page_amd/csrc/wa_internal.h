@@ -106,10 +106,14 @@ AttnPlan attention_plan(int32_t n_heads, int32_t n_q, int32_t n_keys, int cu_cou
 // Sparse branch: per (query block, head) item, the ascending 64-key tiles of
 // [ctx ++ own] to attend over (tiles[item][0 .. count[item])).  tiles == null:
 // every tile (dense attention).
+// The launch plans on the device (whether to split the lists over all CUs);
+// workspace: sparse_workspace_bytes(items, cu_count) bytes.
 struct SparseCtx {
     const int32_t *tiles = nullptr;   // device [items][n_tiles]
     const int32_t *count = nullptr;   // device [items]
+    int cu_count = 0;
 };
+size_t sparse_workspace_bytes(int items, int cu_count);
 
 hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q,
                                  const uint16_t *k_ctx, const uint16_t *v_ctx, int32_t n_ctx,

@@ -303,12 +303,13 @@ def test_paged_attention_rejects(lib):
 # sparse branch (every case below is rejected on the host: nothing launches)
 
 def test_hsa_workspace_size(lib):
-    """fp64 key-block sums [390 context + 74 own blocks][1536] (256-byte
-    aligned), then query-block sums [19][1536], for 49,920 + 4,680 keys and
-    4,680 queries of 12 x 128."""
+    """fp64 key-block sums [390 context + 74 own blocks][1536], query-block
+    sums [19][1536] (each 256-byte aligned), then block scores [19 x 12
+    items][464], for 49,920 + 4,680 keys and 4,680 queries of 12 x 128."""
     kb = (390 + 74) * 1536 * 8
+    qb = 19 * 1536 * 8
     assert lib.wa_hsa_workspace_bytes(L(), 4680, 49920, 4680) == \
-        (kb + 255) // 256 * 256 + 19 * 1536 * 8
+        (kb + 255) // 256 * 256 + (qb + 255) // 256 * 256 + 19 * 12 * 464 * 8
     assert lib.wa_hsa_workspace_bytes(L(), 4680, 49900, 4680) == 0      # n_ctx % 64
     assert lib.wa_hsa_workspace_bytes(L(), 0, 64, 64) == 0
     assert lib.wa_hsa_workspace_bytes(L(), 64, 0, 0) == 0
@@ -352,17 +353,30 @@ def test_hsa_select_rejects(lib):
     assert _hsel(lib, lay=L(dtype=7)) == U
 
 
+def test_sparse_workspace_size(lib):
+    """Plan (256 bytes), list offsets [items + 1] (256-byte aligned), then
+    partial results (256 rows x (128 outputs + max + sum) fp32) for items +
+    CUs slots: 19 query blocks x 12 heads = 228 items, 256 CUs when no device
+    can be queried."""
+    items = 19 * 12
+    assert lib.wa_sparse_workspace_bytes(L(), 4680, 49920, 4680) == \
+        256 + (4 * (items + 1) + 255) // 256 * 256 + (items + 256) * 256 * 130 * 4
+    assert lib.wa_sparse_workspace_bytes(L(dtype=wa.WA_F32), 4680, 49920, 4680) == 0
+    assert lib.wa_sparse_workspace_bytes(L(), 0, 64, 64) == 0
+    assert lib.wa_sparse_workspace_bytes(L(), 64, 64 * 4096, 64) == 0   # 4,097 tiles
+
+
 def _sattn(lib, lay=None, q=A, n_q=64, kc=A, vc=B, n_ctx=64, ko=A, vo=B, n_own=64, scale=0.1,
-           tiles=A, count=B, odt=wa.WA_F32, out=B, lse=NULL):
+           tiles=A, count=B, odt=wa.WA_F32, out=B, lse=NULL, ws=A, ws_bytes=1 << 30):
     return lib.wa_sparse_attention(lay if lay is not None else L(), q, n_q, kc, vc, n_ctx, ko, vo,
-                                   n_own, scale, tiles, count, odt, out, lse, None)
+                                   n_own, scale, tiles, count, odt, out, lse, ws, ws_bytes, None)
 
 
 def test_sparse_attention_rejects(lib):
     """Every argument rule of wa_sparse_attention, one bad argument per call."""
     E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
     assert lib.wa_sparse_attention(None, A, 64, A, B, 64, A, B, 64, 0.1, A, B, wa.WA_F32, B, NULL,
-                                   None) == E
+                                   A, 1 << 30, None) == E
     assert _sattn(lib, tiles=NULL) == E
     assert _sattn(lib, count=NULL) == E
     assert _sattn(lib, tiles=ctypes.c_void_p(0x10002)) == E
@@ -380,3 +394,6 @@ def test_sparse_attention_rejects(lib):
     assert _sattn(lib, lay=L(d=64)) == U                      # head_dim 128
     assert _sattn(lib, odt=5) == U
     assert _sattn(lib, n_ctx=64 * 4096, n_own=64) == U        # 4,097 tiles
+    assert _sattn(lib, ws=NULL) == E                          # workspace missing
+    assert _sattn(lib, ws=MIS) == E
+    assert _sattn(lib, ws_bytes=1024) == E                    # too small

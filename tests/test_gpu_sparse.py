@@ -6,7 +6,9 @@ near tie at the cut and the running sum not within rounding of tau, so that
 one answer is right), the Gini coefficient within fp64 rounding.  Attention
 over the selected tiles: within the attention tolerance of the oracle, and
 bit for bit equal to wa_block_attention where the two do the same arithmetic
-(the full list; one item over a gathered copy of its selected keys).
+(the full list; one item over a gathered copy of its selected keys).  Uneven
+lists at full size are cut into runs over all CUs and merged (the split);
+those cases are held to the oracle.
 """
 import numpy as np
 import pytest
@@ -292,3 +294,64 @@ def test_sparse_full_size():
                                  out_dtype=wa.WA_BF16)
     torch.cuda.synchronize()
     assert np.abs(to_f64(out)[rows] - ref["out"]).max() <= attention_tolerance(wl)
+
+
+def test_full_size_full_list_does_not_split_and_equals_dense():
+    """Every tile of every item at full size (228 items of 854 tiles): even
+    lists, so the launch keeps one workgroup per item, and the output is bit
+    for bit the dense call's."""
+    wl = W.WORKLOADS["wan_kp4"]
+    L = wa_layout(wl)
+    q, kc, vc, ko, vo = _inputs(wl, [11, 3, 14, 7], 49920, 4680, gain=8.0)
+    qd, kcd, vcd, kod, vod = (to_device(x) for x in (q, kc, vc, ko, vo))
+    assert wa.wa_attention_workspace_bytes(L, q.shape[0], 49920, 4680) == 0   # dense: no split
+    tau = torch.full((wl.n_heads,), 2.0, dtype=torch.float64, device="cuda")
+    say("hsa select, full size, keep all")
+    tiles, count, _ = wa.wa_hsa_select(L, qd, kcd, kod, tau, scale=wl.softmax_scale)
+    say("sparse and dense attention, full size, every tile")
+    o_s = wa.wa_sparse_attention(L, qd, kcd, vcd, kod, vod, tiles, count, wl.softmax_scale,
+                                 out_dtype=wa.WA_BF16)
+    o_d = wa.wa_block_attention(L, qd, kcd, vcd, kod, vod, wl.softmax_scale, out_dtype=wa.WA_BF16)
+    torch.cuda.synchronize()
+    assert (count.cpu().numpy() == wa.hsa_shape(L, q.shape[0], 49920, 4680)[2]).all()
+    assert np.array_equal(_bits(o_s), _bits(o_d))
+
+
+def test_split_one_long_list_over_many_blocks():
+    """One head, 320 queries (two items) over 76,800 + 320 keys (1,205 tiles):
+    item 0 lists every tile, item 1 every 30th and the last (ragged) one.  The
+    lists are uneven, so the launch splits them over 64 blocks (19-tile runs)
+    and item 0 is merged from about 64 pieces; sampled rows against the
+    oracle, fp32 and bf16 outputs, with lse."""
+    wl = W.scaled(W.WORKLOADS["wan_kp4"], n_heads=1, frame_tokens=64, page_frames=200,
+                  n_pages=6, chunk_frames=5)
+    L = wa_layout(wl)
+    q, kc, vc, ko, vo = _inputs(wl, list(range(6)), 6 * 12800, 320, gain=0.0)
+    q_blocks, items, n_tiles = wa.hsa_shape(L, q.shape[0], kc.shape[0], ko.shape[0])
+    assert (q_blocks, items, n_tiles) == (2, 2, 1205)
+    lists = [list(range(n_tiles)), sorted(set(range(0, n_tiles, 30)) | {n_tiles - 1})]
+    tiles = np.zeros((items, n_tiles), np.int32)
+    count = np.zeros(items, np.int32)
+    for i, li in enumerate(lists):
+        tiles[i, :len(li)] = li
+        count[i] = len(li)
+    k_all, v_all = np.concatenate([kc, ko]), np.concatenate([vc, vo])
+    n_keys = k_all.shape[0]
+    qd = to_device(q)
+    for odt in (wa.WA_F32, wa.WA_BF16):
+        lse = torch.empty(1, q.shape[0], dtype=torch.float32, device="cuda")
+        say("sparse attention, split over many blocks", odt)
+        out = wa.wa_sparse_attention(L, qd, to_device(kc), to_device(vc), to_device(ko),
+                                     to_device(vo), torch.from_numpy(tiles).cuda(),
+                                     torch.from_numpy(count).cuda(), wl.softmax_scale,
+                                     out_dtype=odt, lse=lse)
+        torch.cuda.synchronize()
+        got, got_lse = to_f64(out), lse.cpu().double().numpy()
+        for i in range(items):
+            keys = np.concatenate([np.arange(64 * t, min(64 * t + 64, n_keys)) for t in lists[i]])
+            rows = np.arange(256 * i, min(256 * (i + 1), q.shape[0]))[::23]
+            ref, ref_lse = oracle.attention(q, np.ascontiguousarray(k_all[keys]),
+                                            np.ascontiguousarray(v_all[keys]), None, None,
+                                            wl.softmax_scale, rows=rows)
+            assert np.abs(got[rows] - ref).max() <= attention_tolerance(wl)
+            assert np.abs(got_lse[:, rows] - ref_lse).max() <= attention_tolerance(wl)
