@@ -16,7 +16,12 @@ the order the pages give them:
 * attention over [cached ++ own] K/V with one softmax and no mask -- Inferix
   summary, section 3.4, "The Block-Diffusion Generation Pipeline", Step 3;
   softmax and value weighting after the score contraction -- the einsum post,
-  "Where the mental model stops".
+  "Where the mental model stops";
+* the sparse branch (key blocks, pooled attention map, Gini coefficient,
+  cumulative-mass block selection, attention over the selected blocks) --
+  WorldAttention review, "HSA: Dual Branches of Linear + Sparse"; these
+  compose the C attention with numpy, and their pins are planted with
+  mistakes in ``tests/test_oracle_mutations_hsa.py``.
 
 Parity status of each function: pinned by ``tests/test_oracle_pins.py``
 (closed forms, invariants, brute force, and a textbook library routine).

@@ -389,6 +389,8 @@ def test_select_blocks_is_the_fewest_by_brute_force(oracle_lib, n):
     mass = np.array([0.1, 0.5, 0.2, 0.2])
     assert oracle_lib.select_blocks(mass, 0.3) == [1]                    # the largest alone
     assert oracle_lib.select_blocks(mass, 2.0) == [0, 1, 2, 3]            # unreachable: all
+    assert oracle_lib.select_blocks(mass, 0.0) == [1]                    # at least one block
+    assert oracle_lib.select_blocks(mass, -1.0) == [1]
     assert oracle_lib.select_blocks(mass, 0.7) == [1, 2]                  # tie 0.2/0.2 -> lower index
 
 
@@ -447,3 +449,17 @@ def test_hsa_one_block_is_softmax_over_its_keys(oracle_lib):
             want = (p[:, None] * v_all[a:z, h]).sum(axis=0) / p.sum()
             assert np.abs(r["out"][i, h] - want).max() < 1e-12
             assert abs(r["lse"][h, i] - (s.max() + np.log(p.sum()))) < 1e-12
+
+
+def test_hsa_threshold_is_per_head(oracle_lib):
+    """tau = [tiny, above 1]: head 0 keeps exactly the argmax block of its own
+    map, head 1 keeps every block, in every query block."""
+    q, kc, vc, ko, vo = _hsa_inputs()
+    r = oracle_lib.hsa_sparse(q, kc, vc, ko, vo, 0.25, [1e-12, 2.0])
+    nb = len(r["blocks"])
+    for (h, b), chosen in r["sel"].items():
+        pmap = r["maps"][b][h]
+        if h == 0:
+            assert chosen == [int(np.argmax(pmap))]
+        else:
+            assert chosen == list(range(nb))
