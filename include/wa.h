@@ -19,7 +19,9 @@
  *   wa_hsa_select      the sparse branch's block selection: per head and
  *                      query block, the fewest key blocks that hold a given
  *                      share of a pooled attention map;
- *   wa_sparse_attention attention over those blocks only.
+ *   wa_sparse_attention attention over those blocks only;
+ *   wa_page_in/out     move a page between a pinned host tier and HBM;
+ *   wa_merge_attention combine attentions over two disjoint key sets.
  *
  * Sources (page title, section):
  *   WorldAttention review, "WorldAttention: An Efficient Attention
@@ -383,6 +385,59 @@ wa_status wa_sparse_attention(const wa_layout *layout, const void *q, int32_t n_
  * pieces.  Launches nothing. */
 size_t wa_sparse_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ctx,
                                  int32_t n_own);
+
+/*
+ * Host-memory page tier (WorldAttention review, "HKV: Page-Level Multi-Tier
+ * Memory": tier L1 (HBM) holds the retrieved pages, tier L2 (host DRAM) the
+ * pages the current chunk does not use; Inferix summary, "KV Cache Manager",
+ * offloading to main memory: a block fetched by index is loaded back into GPU
+ * memory before the attention).  The caller keeps the page table (which
+ * logical page is in which HBM slot or host slot) and the policy; these calls
+ * move pages between tiers.
+ *
+ * wa_page_in:  k_pool[slot] = host_k[host_slot] (and V), host -> HBM;
+ * wa_page_out: host_k[host_slot] = k_pool[slot] (and V), HBM -> host.
+ * host_k, host_v: PINNED host memory from hipHostMalloc, [host_pages]
+ * [page_tokens][H][d] in layout.dtype, owned by the caller; pageable memory is
+ * rejected.  host_v and v_pool may both be NULL (K only).  The copies are
+ * queued on `stream` for the copy engines (no kernel runs, nothing is
+ * allocated) and run asynchronously: the caller orders them against the
+ * attention that reads the slot with stream order or events, and must keep
+ * the host pool unchanged until a page-in has finished.  Page means are not
+ * touched (they stay in HBM for every page, so selection sees every tier).
+ * Errors: NULL layout / host_k / k_pool, only one of host_v / v_pool NULL,
+ * host_slot outside [0, host_pages), slot outside [0, max_pages), misaligned
+ * pointers, a host pool that is not pinned host memory -> WA_ERR_INVALID_ARG;
+ * a failed copy -> WA_ERR_HIP.
+ */
+wa_status wa_page_in(const wa_layout *layout, const void *host_k, const void *host_v,
+                     int32_t host_pages, int32_t host_slot, void *k_pool, void *v_pool,
+                     int32_t slot, void *stream);
+wa_status wa_page_out(const wa_layout *layout, const void *k_pool, const void *v_pool,
+                      int32_t slot, void *host_k, void *host_v, int32_t host_pages,
+                      int32_t host_slot, void *stream);
+
+/*
+ * Merge of two attentions of the same queries over disjoint key sets A and B
+ * (Inferix summary, "Ring Attention": partial attention over one chunk of keys
+ * at a time, accumulated; here A = the pages resident in HBM, B = the pages
+ * brought in from host memory, so that the attention over A runs while B is
+ * copied).  For head h and query i, with lse_X = log sum_{n in X} exp(s_n):
+ *   lse[h][i] = log(exp(lse_A) + exp(lse_B))
+ *   out[i][h] = exp(lse_A - lse) out_A[i][h] + exp(lse_B - lse) out_B[i][h]
+ * which is the attention over A u B (wa_block_attention's definition).
+ * out_a, out_b: fp32 [n_q][H][d] (attention outputs with WA_F32 out_dtype);
+ * lse_a, lse_b: fp32 [H][n_q], at least one of each pair finite; out:
+ * [n_q][H][d] in out_dtype (WA_F32 or WA_BF16); lse: [H][n_q] or NULL.  out
+ * may be out_a when out_dtype is WA_F32; no other overlap.  head_dim must be
+ * a multiple of 4.
+ * Errors: NULL layout / out_a / lse_a / out_b / lse_b / out, n_q < 1,
+ * misaligned pointers -> WA_ERR_INVALID_ARG; out_dtype, head_dim % 4 != 0 ->
+ * WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_merge_attention(const wa_layout *layout, int32_t n_q, const float *out_a,
+                             const float *lse_a, const float *out_b, const float *lse_b,
+                             int32_t out_dtype, void *out, float *lse, void *stream);
 
 /* Static text describing a status code. */
 const char *wa_status_string(wa_status status);

@@ -17,6 +17,9 @@ the order the pages give them:
   summary, section 3.4, "The Block-Diffusion Generation Pipeline", Step 3;
   softmax and value weighting after the score contraction -- the einsum post,
   "Where the mental model stops";
+* the merge of two attentions over disjoint key sets -- Inferix summary,
+  "Ring Attention" (partial attention over one chunk of keys at a time,
+  accumulated), used for the host-memory page tier;
 * the sparse branch (key blocks, pooled attention map, Gini coefficient,
   cumulative-mass block selection, attention over the selected blocks) --
   WorldAttention review, "HSA: Dual Branches of Linear + Sparse"; these
@@ -340,6 +343,20 @@ def hsa_sparse(q, k_ctx, v_ctx, k_own, v_own, scale: float, tau, q_block: int = 
             out[mine, h] = o[:, 0]
             lse[h, mine] = l[0]
     return dict(out=out, lse=lse, sel=sel, gini=gin, maps=maps, blocks=blocks)
+
+
+def merge_attention(out_a, lse_a, out_b, lse_b):
+    """Attention over A u B from attentions over disjoint key sets A and B
+    (outputs [n, H, d], lse [H, n], natural log): the softmax over the union
+    weights each part by its share of the total, exp(lse_X - lse), with
+    lse = log(exp(lse_A) + exp(lse_B)); taken against the larger lse."""
+    oa, ob = np.asarray(out_a, np.float64), np.asarray(out_b, np.float64)
+    la, lb = np.asarray(lse_a, np.float64), np.asarray(lse_b, np.float64)
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    tot = wa + wb
+    out = (wa / tot).T[:, :, None] * oa + (wb / tot).T[:, :, None] * ob
+    return out, m + np.log(tot)
 
 
 def boundary_margin(alpha: np.ndarray, k_p: int) -> float:

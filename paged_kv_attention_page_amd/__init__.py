@@ -26,7 +26,7 @@ __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "W
            "wa_select_pages", "wa_select_window", "wa_gather", "wa_attention_workspace_bytes",
            "wa_block_attention", "wa_paged_attention", "hsa_shape", "wa_hsa_workspace_bytes",
            "wa_hsa_select", "wa_sparse_workspace_bytes", "wa_sparse_attention",
-           "wa_status_string"]
+           "wa_page_in", "wa_page_out", "wa_merge_attention", "wa_status_string"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -113,6 +113,12 @@ def load_library():
     lib.wa_hsa_select.restype = i32
     lib.wa_sparse_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, p, p, i32, p, p, p,
                                         sz, p]
+    lib.wa_page_in.argtypes = [L, p, p, i32, i32, p, p, i32, p]
+    lib.wa_page_in.restype = i32
+    lib.wa_page_out.argtypes = [L, p, p, i32, p, p, i32, i32, p]
+    lib.wa_page_out.restype = i32
+    lib.wa_merge_attention.argtypes = [L, i32, p, p, p, p, i32, p, p, p]
+    lib.wa_merge_attention.restype = i32
     lib.wa_sparse_workspace_bytes.argtypes = [L, i32, i32, i32]
     lib.wa_sparse_workspace_bytes.restype = sz
     lib.wa_sparse_attention.restype = i32
@@ -496,4 +502,67 @@ def wa_sparse_attention(L: Layout, q, k_ctx, v_ctx, k_own, v_own, sel_tiles, sel
                                  int(out_dtype), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                  _stream(stream))
     _check(st, "wa_sparse_attention")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# host-memory page tier
+
+def _host_pool(t, name, L):
+    if t is None:
+        return 0
+    _need(t, name, L.torch_dtype, device=False)
+    if not t.is_pinned():
+        raise ValueError("%s must be pinned host memory (pin_memory=True)" % name)
+    page = L.page_tokens * L.row_elems
+    if t.numel() % page:
+        raise ValueError("%s is not a whole number of pages" % name)
+    return t.numel() // page
+
+
+def wa_page_in(L: Layout, host_k, host_v, host_slot: int, k_pool, v_pool, slot: int,
+               stream=None):
+    """k_pool[slot] = host_k[host_slot] (and V), queued on the copy engines."""
+    lib = load_library()
+    n = _host_pool(host_k, "host_k", L)
+    if host_v is not None and _host_pool(host_v, "host_v", L) != n:
+        raise ValueError("host_k and host_v hold different page counts")
+    st = lib.wa_page_in(ctypes.byref(L), _ptr(host_k), _ptr(host_v), int(n), int(host_slot),
+                        _ptr(k_pool), _ptr(v_pool), int(slot), _stream(stream))
+    _check(st, "wa_page_in")
+
+
+def wa_page_out(L: Layout, k_pool, v_pool, slot: int, host_k, host_v, host_slot: int,
+                stream=None):
+    """host_k[host_slot] = k_pool[slot] (and V), queued on the copy engines."""
+    lib = load_library()
+    n = _host_pool(host_k, "host_k", L)
+    if host_v is not None and _host_pool(host_v, "host_v", L) != n:
+        raise ValueError("host_k and host_v hold different page counts")
+    st = lib.wa_page_out(ctypes.byref(L), _ptr(k_pool), _ptr(v_pool), int(slot), _ptr(host_k),
+                         _ptr(host_v), int(n), int(host_slot), _stream(stream))
+    _check(st, "wa_page_out")
+
+
+def wa_merge_attention(L: Layout, out_a, lse_a, out_b, lse_b, out_dtype=WA_F32, out=None,
+                       lse=None, stream=None):
+    """Attention over A u B from the attentions over A and over B (fp32
+    outputs with their lse); returns out [n_q, H, d]."""
+    lib = load_library()
+    row = L.row_elems
+    _need(out_a, "out_a", torch.float32)
+    n_q = out_a.numel() // row
+    _need(out_b, "out_b", torch.float32, n_q * row)
+    _need(lse_a, "lse_a", torch.float32, n_q * L.n_heads)
+    _need(lse_b, "lse_b", torch.float32, n_q * L.n_heads)
+    odt = _TORCH_DTYPE[out_dtype]
+    if out is None:
+        out = torch.empty((n_q, L.n_heads, L.head_dim), dtype=odt, device=out_a.device)
+    _need(out, "out", odt, n_q * row)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, n_q * L.n_heads)
+    st = lib.wa_merge_attention(ctypes.byref(L), int(n_q), _ptr(out_a), _ptr(lse_a), _ptr(out_b),
+                                _ptr(lse_b), int(out_dtype), _ptr(out), _ptr(lse),
+                                _stream(stream))
+    _check(st, "wa_merge_attention")
     return out

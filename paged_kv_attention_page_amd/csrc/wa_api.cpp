@@ -300,6 +300,79 @@ wa_status wa_sparse_attention(const wa_layout *L, const void *q, int32_t n_q, co
                      out_dtype, out, lse, workspace, ws_bytes, PagedCtx{}, stream, sp);
 }
 
+wa_status wa_merge_attention(const wa_layout *L, int32_t n_q, const float *out_a,
+                             const float *lse_a, const float *out_b, const float *lse_b,
+                             int32_t out_dtype, void *out, float *lse, void *stream) {
+    const wa_status st = check_layout(L, false);
+    if (st != WA_OK) return st;
+    if (!out_a || !lse_a || !out_b || !lse_b || !out) return WA_ERR_INVALID_ARG;
+    if (n_q < 1) return WA_ERR_INVALID_ARG;
+    if (!aligned16(out_a) || !aligned16(out_b) || !aligned16(out) || ((uintptr_t)lse_a & 3u) ||
+        ((uintptr_t)lse_b & 3u) || ((uintptr_t)lse & 3u))
+        return WA_ERR_INVALID_ARG;
+    if (out_dtype != WA_F32 && out_dtype != WA_BF16) return WA_ERR_UNSUPPORTED;
+    if (L->head_dim % 4 != 0) return WA_ERR_UNSUPPORTED;
+    return from_hip(launch_merge_attention(L->n_heads, L->head_dim, n_q, out_a, lse_a, out_b,
+                                           lse_b, out_dtype, out, lse, (hipStream_t)stream));
+}
+
+namespace {
+
+// One page of K (and V) between a pinned host pool and an HBM pool slot, on
+// the caller's stream (the copy engines move it; no kernel runs).
+wa_status page_copy(const wa_layout *L, bool to_device, const void *host_k, const void *host_v,
+                    int32_t host_pages, int32_t host_slot, const void *k_pool, const void *v_pool,
+                    int32_t slot, void *stream) {
+    const wa_status st = check_layout(L, true);
+    if (st != WA_OK) return st;
+    if (!host_k || !k_pool) return WA_ERR_INVALID_ARG;
+    if ((host_v == nullptr) != (v_pool == nullptr)) return WA_ERR_INVALID_ARG;
+    if (host_pages < 1 || host_slot < 0 || host_slot >= host_pages) return WA_ERR_INVALID_ARG;
+    if (slot < 0 || slot >= L->max_pages) return WA_ERR_INVALID_ARG;
+    if (!aligned16(host_k) || !aligned16(k_pool) || (host_v && !aligned16(host_v)) ||
+        (v_pool && !aligned16(v_pool)))
+        return WA_ERR_INVALID_ARG;
+    // the host pool must be pinned host memory (hipHostMalloc): pageable
+    // memory would turn the asynchronous copy into a staged, blocking one
+    for (const void *h : {host_k, host_v}) {
+        if (!h) continue;
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, h) != hipSuccess) {
+            (void)hipGetLastError();
+            return WA_ERR_INVALID_ARG;
+        }
+        if (attr.type != hipMemoryTypeHost) return WA_ERR_INVALID_ARG;
+    }
+    const size_t page_bytes =
+        (size_t)L->page_tokens * L->n_heads * L->head_dim * elem_bytes(L->dtype);
+    const hipMemcpyKind kind = to_device ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+    const char *hk = (const char *)host_k + (size_t)host_slot * page_bytes;
+    const char *dk = (const char *)k_pool + (size_t)slot * page_bytes;
+    hipError_t e = to_device ? hipMemcpyAsync((void *)dk, hk, page_bytes, kind, (hipStream_t)stream)
+                             : hipMemcpyAsync((void *)hk, dk, page_bytes, kind, (hipStream_t)stream);
+    if (e != hipSuccess || !host_v) return from_hip(e);
+    const char *hv = (const char *)host_v + (size_t)host_slot * page_bytes;
+    const char *dv = (const char *)v_pool + (size_t)slot * page_bytes;
+    e = to_device ? hipMemcpyAsync((void *)dv, hv, page_bytes, kind, (hipStream_t)stream)
+                  : hipMemcpyAsync((void *)hv, dv, page_bytes, kind, (hipStream_t)stream);
+    return from_hip(e);
+}
+
+}  // namespace
+
+wa_status wa_page_in(const wa_layout *L, const void *host_k, const void *host_v,
+                     int32_t host_pages, int32_t host_slot, void *k_pool, void *v_pool,
+                     int32_t slot, void *stream) {
+    return page_copy(L, true, host_k, host_v, host_pages, host_slot, k_pool, v_pool, slot, stream);
+}
+
+wa_status wa_page_out(const wa_layout *L, const void *k_pool, const void *v_pool, int32_t slot,
+                      void *host_k, void *host_v, int32_t host_pages, int32_t host_slot,
+                      void *stream) {
+    return page_copy(L, false, host_k, host_v, host_pages, host_slot, k_pool, v_pool, slot,
+                     stream);
+}
+
 const char *wa_status_string(wa_status s) {
     switch (s) {
         case WA_OK: return "ok";

@@ -122,6 +122,12 @@ hipError_t launch_attention_bf16(int32_t n_heads, const uint16_t *q, int32_t n_q
                                  const AttnPlan &plan, void *workspace, const PagedCtx &pg,
                                  hipStream_t s, const SparseCtx &sp = SparseCtx{});
 
+// merge of two attentions over disjoint key sets (fp32 outputs and lse)
+hipError_t launch_merge_attention(int32_t n_heads, int32_t head_dim, int32_t n_q,
+                                  const float *out_a, const float *lse_a, const float *out_b,
+                                  const float *lse_b, int32_t out_dtype, void *out, float *lse,
+                                  hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // sparse branch block selection
 

@@ -397,3 +397,56 @@ def test_sparse_attention_rejects(lib):
     assert _sattn(lib, ws=NULL) == E                          # workspace missing
     assert _sattn(lib, ws=MIS) == E
     assert _sattn(lib, ws_bytes=1024) == E                    # too small
+
+
+# ---------------------------------------------------------------------------
+# host-memory page tier and the merge (rejected on the host: nothing runs)
+
+def _pin(lib, fn="wa_page_in", lay=None, hk=A, hv=B, host_pages=4, host_slot=1, kp=A, vp=B,
+         slot=2):
+    f = getattr(lib, fn)
+    lay = None if lay == "null" else (lay if lay is not None else L())
+    if fn == "wa_page_in":
+        return f(lay, hk, hv, host_pages, host_slot, kp, vp, slot, None)
+    return f(lay, kp, vp, slot, hk, hv, host_pages, host_slot, None)
+
+
+@pytest.mark.parametrize("fn", ["wa_page_in", "wa_page_out"])
+def test_page_copy_rejects(lib, fn):
+    """Every argument rule of wa_page_in / wa_page_out, one bad argument per
+    call; the last case passes every other check with a host pointer that is
+    not pinned host memory (a stand-in address), so nothing is copied."""
+    E = wa.WA_ERR_INVALID_ARG
+    assert _pin(lib, fn, lay="null") == E
+    assert _pin(lib, fn, hk=NULL) == E
+    assert _pin(lib, fn, kp=NULL) == E
+    assert _pin(lib, fn, hv=NULL) == E                      # one of host_v / v_pool
+    assert _pin(lib, fn, vp=NULL) == E
+    assert _pin(lib, fn, host_pages=0) == E
+    assert _pin(lib, fn, host_slot=-1) == E
+    assert _pin(lib, fn, host_slot=4) == E
+    assert _pin(lib, fn, slot=-1) == E
+    assert _pin(lib, fn, slot=16) == E
+    assert _pin(lib, fn, lay=L(pt=0)) == E
+    assert _pin(lib, fn, hk=MIS) == E
+    assert _pin(lib, fn, vp=MIS) == E
+    assert _pin(lib, fn) == E                               # not pinned host memory
+
+
+def _merge(lib, lay=None, n_q=64, oa=A, la=B, ob=A, lb=B, odt=wa.WA_F32, out=B, lse=NULL):
+    return lib.wa_merge_attention(lay if lay is not None else L(), n_q, oa, la, ob, lb, odt, out,
+                                  lse, None)
+
+
+def test_merge_attention_rejects(lib):
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert lib.wa_merge_attention(None, 64, A, B, A, B, wa.WA_F32, B, NULL, None) == E
+    for bad in ("oa", "la", "ob", "lb", "out"):
+        assert _merge(lib, **{bad: NULL}) == E, bad
+    assert _merge(lib, n_q=0) == E
+    assert _merge(lib, oa=MIS) == E
+    assert _merge(lib, out=MIS) == E
+    assert _merge(lib, la=ctypes.c_void_p(0x10002)) == E
+    assert _merge(lib, lse=ctypes.c_void_p(0x10002)) == E
+    assert _merge(lib, odt=7) == U
+    assert _merge(lib, lay=L(d=30)) == U                     # head_dim % 4

@@ -1,6 +1,7 @@
-"""Plant plausible mistakes in the sparse-branch functions of the oracle (the
-Python part of ``oracle/__init__.py``: key blocks, Gini coefficient, block
-selection, pooled map, composition) and check that the pins catch each one.
+"""Plant plausible mistakes in the functions the oracle writes in Python
+(``oracle/__init__.py``: the sparse branch's key blocks, Gini coefficient,
+block selection, pooled map and composition; the merge of two attentions)
+and check that the pins catch each one.
 
 Each mutation is a textual edit of a copy of the module, loaded under another
 name over the same compiled library; every pin of ``test_oracle_pins`` runs
@@ -39,6 +40,13 @@ MUTATIONS = {
                                            "chosen = select_blocks(pmap[h], float(tau[0]))"),
     "every head uses head 0's map": ("chosen = select_blocks(pmap[h], float(tau[h]))",
                                      "chosen = select_blocks(pmap[0], float(tau[h]))"),
+    "merge weights the parts the wrong way round": (
+        "out = (wa / tot).T[:, :, None] * oa + (wb / tot).T[:, :, None] * ob",
+        "out = (wb / tot).T[:, :, None] * oa + (wa / tot).T[:, :, None] * ob"),
+    "merge forgets to normalise the weights": (
+        "out = (wa / tot).T[:, :, None] * oa + (wb / tot).T[:, :, None] * ob",
+        "out = wa.T[:, :, None] * oa + wb.T[:, :, None] * ob"),
+    "merge lse drops the max": ("    return out, m + np.log(tot)", "    return out, np.log(tot)"),
 }
 
 
@@ -64,7 +72,7 @@ def test_unmutated_copy_passes_every_pin(tmp_path):
 
 
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS))
-def test_pins_catch_planted_mistake_in_sparse_branch(mutation, tmp_path):
+def test_pins_catch_planted_mistake_in_python_part(mutation, tmp_path):
     old, new = MUTATIONS[mutation]
     text = open(SRC).read()
     assert text.count(old) == 1, "mutation anchor not found once: %r" % old

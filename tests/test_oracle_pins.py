@@ -463,3 +463,31 @@ def test_hsa_threshold_is_per_head(oracle_lib):
             assert chosen == [int(np.argmax(pmap))]
         else:
             assert chosen == list(range(nb))
+
+
+@pytest.mark.parametrize("cut", [1, 37, 64, 90])
+def test_merge_of_two_key_sets_is_attention_over_their_union(oracle_lib, cut):
+    """Attention over keys [0, cut) merged with attention over [cut, n) equals
+    the attention over all n keys (computed in one piece by the C oracle)."""
+    rng = np.random.default_rng(11)
+    n, H, d, nq = 100, 2, 16, 9
+    q = rng.standard_normal((nq, H, d)).astype(np.float32)
+    k = (2.0 * rng.standard_normal((n, H, d))).astype(np.float32)
+    v = rng.standard_normal((n, H, d)).astype(np.float32)
+    full, lse = oracle_lib.attention(q, k, v, None, None, 0.3)
+    oa, la = oracle_lib.attention(q, k[:cut], v[:cut], None, None, 0.3)
+    ob, lb = oracle_lib.attention(q, k[cut:], v[cut:], None, None, 0.3)
+    out, l = oracle_lib.merge_attention(oa, la, ob, lb)
+    assert np.abs(out - full).max() < 1e-12 and np.abs(l - lse).max() < 1e-12
+    out2, l2 = oracle_lib.merge_attention(ob, lb, oa, la)        # order of the parts
+    assert np.abs(out2 - full).max() < 1e-12 and np.abs(l2 - lse).max() < 1e-12
+
+
+def test_merge_with_an_empty_part_is_the_other_part(oracle_lib):
+    rng = np.random.default_rng(12)
+    oa = rng.standard_normal((5, 2, 8))
+    la = rng.standard_normal((2, 5)) + 40.0        # large lse: no overflow
+    ob = rng.standard_normal((5, 2, 8))
+    lb = np.full((2, 5), -np.inf)
+    out, l = oracle_lib.merge_attention(oa, la, ob, lb)
+    assert np.array_equal(out, oa) and np.array_equal(l, la)
