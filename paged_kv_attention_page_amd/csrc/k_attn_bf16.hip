@@ -64,6 +64,13 @@ static constexpr int kCopies = kRowsPerWave / 4;    // 1 KB copies per tensor pe
 // probabilities recomputed.  The result is exact either way, since O and l
 // always share the reference max, and no per-sub-tile maximum is needed.
 static constexpr float kSumLimit = 256.f;
+// LDS operands are read this many matrix products ahead of their use (of the
+// 8 per region); 2, 4, 5, 6, 7 and 8 measured 1.38, 1.37, 1.36, 1.36, 1.41
+// and 1.40 ms on the Wan-shaped launch: 6 hides the LDS latency best within
+// the register budget.  The tile-list mode keeps more state live across the
+// loop and uses a shorter distance so that it does not spill.
+static constexpr int kPrefetch = 6;
+static constexpr int kPrefetchLists = 2;
 static constexpr int kMaxSplitBlocks = 256;  // blocks of a split launch (partial slots)
 static constexpr int kMinSplitTiles = 16;    // fewest tiles per block worth a split
 static constexpr int kMaxBlocksPerItem = 32; // split blocks per (query block, head) item
@@ -249,6 +256,7 @@ void k_attn_bf16(AttnArgs a) {
     const int n_tiles = a.n_tiles;
     const bool ragged = (n_keys % kBN) != 0;
     const float c = a.c;
+    constexpr int kPf = MODE == 3 ? kPrefetchLists : kPrefetch;
 
     // ---- tile loads: wavefront w copies rows 8w ... 8w+7 of the K and V
     // tiles, 4 rows (1 KB) per instruction; lane -> (row 8w+4i+lane/16, slot lane%16)
@@ -443,9 +451,10 @@ void k_attn_bf16(AttnArgs a) {
     // ---- region QK+SOFTMAX: sn = K Q^T of the sub-tile at koff (8 MFMAs)
     // interleaved with the exponentials of sc (2 elements per MFMA), P packed to
     // bf16 for the P V products, l accumulated from the bf16 values; then the
-    // lazy-rescale test (see kSumLimit).  ak[0], ak[1] arrive prefetched; the
-    // V^T operands 0 and 1 of the following P V region (at voff) are prefetched
-    // at the end.
+    // lazy-rescale test (see kSumLimit).  Operands are read kPf products
+    // ahead: ak[0 .. kPf) arrive prefetched, and the first kPf V^T
+    // operands of the following P V region (at voff) are read during the last
+    // products of this one.
     auto qk_softmax = [&](int koff, f32x16 &sn, const f32x16 &sc, bf16x8 (&pb)[2],
                           bf16x8 (&ak)[8], int voff, bf16x8 (&av)[8]) __attribute__((always_inline)) {
         const float mc = m * c;
@@ -462,8 +471,8 @@ void k_attn_bf16(AttnArgs a) {
             pb[st >> 2][2 * (st & 3) + 1] = pr[1];
             if (st & 1) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls1, false);
             else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls0, false);
-            if (st + 2 < 8) ak[st + 2] = read_k(koff, st + 2);
-            if (st >= 6) av[st - 6] = read_v(voff, st - 6);
+            if (st + kPf < 8) ak[st + kPf] = read_k(koff, st + kPf);
+            if (st >= 8 - kPf) av[st - (8 - kPf)] = read_v(voff, st - (8 - kPf));
         }
         float lsub = ls0 + ls1;
         if (__builtin_amdgcn_ballot_w64(lsub > kSumLimit) != 0) {
@@ -494,17 +503,17 @@ void k_attn_bf16(AttnArgs a) {
         l += lsub;
     };
 
-    // ---- region PV: O^T += V^T P^T (8 MFMAs); prefetches the next V^T
-    // operands two steps ahead and, at the end, the first two K operands of the
-    // next QK+SOFTMAX region.
+    // ---- region PV: O^T += V^T P^T (8 MFMAs); reads the V^T operands
+    // kPf products ahead and, during its last products, the first
+    // kPf K operands of the next QK+SOFTMAX region.
     auto pv = [&](int voff, const bf16x8 (&pb)[2], bf16x8 (&av)[8], int koff_next,
                   bf16x8 (&ak)[8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int op = 0; op < 8; ++op) {
             const int jj = op >> 2, b = op & 3;
             o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[op], pb[jj], o[b], 0, 0, 0);
-            if (op + 2 < 8) av[op + 2] = read_v(voff, op + 2);
-            if (op >= 6) ak[op - 6] = read_k(koff_next, op - 6);
+            if (op + kPf < 8) av[op + kPf] = read_v(voff, op + kPf);
+            if (op >= 8 - kPf) ak[op - (8 - kPf)] = read_k(koff_next, op - (8 - kPf));
         }
     };
 
@@ -542,8 +551,8 @@ void k_attn_bf16(AttnArgs a) {
         for (int st = 0; st < 8; ++st)
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sa, 0, 0, 0);
         if (t_begin == mask_tile) mask_tail(sa, mask_key0);
-        ak[0] = read_k(kSubBytes, 0);
-        ak[1] = read_k(kSubBytes, 1);
+#pragma unroll
+        for (int st = 0; st < kPf; ++st) ak[st] = read_k(kSubBytes, st);
     }
 
     // Tile t in stage S; on entry sa = S(t, 0) with the reference max already
