@@ -355,3 +355,36 @@ def test_split_one_long_list_over_many_blocks():
                                             wl.softmax_scale, rows=rows)
             assert np.abs(got[rows] - ref).max() <= attention_tolerance(wl)
             assert np.abs(got_lse[:, rows] - ref_lse).max() <= attention_tolerance(wl)
+
+
+def test_more_items_than_compute_units():
+    """12 heads x 24 query blocks = 288 items (more than the 256 CUs: the
+    launch plans in rounds) over 4 pages of 1,024 keys plus 6,144 own keys,
+    thresholds that differ by head; selection of three query blocks and
+    sampled rows of the output against the oracle."""
+    wl = W.scaled(W.WORKLOADS["wan_kp4"], frame_tokens=128, page_frames=8, n_pages=4,
+                  chunk_frames=48)
+    L = wa_layout(wl)
+    q, kc, vc, ko, vo = _inputs(wl, [3, 0, 2, 1], 4096, wl.n_q, gain=8.0)
+    q_blocks, items, n_tiles = wa.hsa_shape(L, q.shape[0], 4096, wl.n_q)
+    assert (q_blocks, items) == (24, 288)
+    tau = [0.3 + 0.06 * h for h in range(wl.n_heads)]
+    tau_d = torch.tensor(tau, dtype=torch.float64, device="cuda")
+    say("hsa select, 288 items")
+    tiles, count, gini = wa.wa_hsa_select(L, to_device(q), to_device(kc), to_device(ko), tau_d,
+                                          scale=wl.softmax_scale)
+    say("sparse attention, 288 items")
+    out = wa.wa_sparse_attention(L, to_device(q), to_device(kc), to_device(vc), to_device(ko),
+                                 to_device(vo), tiles, count, wl.softmax_scale,
+                                 out_dtype=wa.WA_F32)
+    torch.cuda.synchronize()
+    tiles, count, gini = tiles.cpu().numpy(), count.cpu().numpy(), gini.cpu().numpy()
+    rows = np.concatenate([np.arange(0, 256, 37), np.arange(256 * 11, 256 * 12, 37),
+                           np.arange(256 * 23, q.shape[0], 37), [q.shape[0] - 1]])
+    ref = oracle.hsa_sparse(q, kc, vc, ko, vo, wl.softmax_scale, tau, rows=rows)
+    for (h, b), chosen in ref["sel"].items():
+        item = h * q_blocks + b
+        _clear_cut(ref["maps"][b][h], tau[h])
+        assert tiles[item, :count[item]].tolist() == _tiles_of(ref["blocks"], chosen)
+        assert abs(gini[item] - ref["gini"][(h, b)]) <= 1e-12
+    assert np.abs(to_f64(out)[rows] - ref["out"]).max() <= attention_tolerance(wl)
