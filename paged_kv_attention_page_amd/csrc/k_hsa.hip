@@ -19,10 +19,11 @@
 //                 workgroup from LDS, so that each key-block mean is read
 //                 once per 16 query blocks.
 //   k_hsa_select  one workgroup per (head, query block): softmax of its
-//                 scores, each block's rank in the order (mass desc, block
-//                 asc), the Gini coefficient, the shortest prefix in that
-//                 order whose running sum reaches tau_h (at least one block),
-//                 and the selected blocks' 64-key tiles in ascending order.
+//                 scores, a bitonic sort into (mass desc, block asc) in the
+//                 registers of one wavefront, the Gini coefficient, the
+//                 shortest prefix in that order whose running sum reaches
+//                 tau_h (at least one block), and the selected blocks' 64-key
+//                 tiles in ascending order.
 #include <math.h>
 
 #include "colsum.h"
@@ -35,7 +36,7 @@ static constexpr int kHsaIntra = WA_HSA_OWN_BLOCK;   // keys per own block
 static constexpr int kHsaQBlock = WA_HSA_Q_BLOCK;    // queries per pooled query block
 static constexpr int kHsaRowLanes = 4;               // column-sum row lanes
 static constexpr int kHsaThreads = 256;
-static_assert(WA_MAX_HSA_BLOCKS % kHsaThreads == 0, "block ownership");
+static_assert(WA_MAX_HSA_BLOCKS <= 64 * 32, "the sort holds at most 32 blocks per lane");
 
 HsaShape hsa_shape(int32_t n_heads, int32_t n_q, int32_t n_ctx, int32_t n_own) {
     HsaShape w;
