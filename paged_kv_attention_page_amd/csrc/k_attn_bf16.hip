@@ -67,10 +67,8 @@ static constexpr float kSumLimit = 256.f;
 // LDS operands are read this many matrix products ahead of their use (of the
 // 8 per region); 2, 4, 5, 6, 7 and 8 measured 1.38, 1.37, 1.36, 1.36, 1.41
 // and 1.40 ms on the Wan-shaped launch: 6 hides the LDS latency best within
-// the register budget.  The tile-list mode keeps more state live across the
-// loop and uses a shorter distance so that it does not spill.
+// the register budget.
 static constexpr int kPrefetch = 6;
-static constexpr int kPrefetchLists = 2;
 static constexpr int kMaxSplitBlocks = 256;  // blocks of a split launch (partial slots)
 static constexpr int kMinSplitTiles = 16;    // fewest tiles per block worth a split
 static constexpr int kMaxBlocksPerItem = 32; // split blocks per (query block, head) item
@@ -256,7 +254,7 @@ void k_attn_bf16(AttnArgs a) {
     const int n_tiles = a.n_tiles;
     const bool ragged = (n_keys % kBN) != 0;
     const float c = a.c;
-    constexpr int kPf = MODE == 3 ? kPrefetchLists : kPrefetch;
+    constexpr int kPf = kPrefetch;
 
     // ---- tile loads: wavefront w copies rows 8w ... 8w+7 of the K and V
     // tiles, 4 rows (1 KB) per instruction; lane -> (row 8w+4i+lane/16, slot lane%16)
@@ -671,7 +669,10 @@ void k_attn_bf16(AttnArgs a) {
             const int e = p1 < g1 ? p1 : g1;
             __syncthreads();   // every wave is done with the previous piece's list
             load_list(lo, g - p0, e - p0);
-            segment(lo, 0, e - g, (g == p0 && e == p1) ? -1 : lo + blk);
+            // (the arguments made uniform, as in the dense split: the compiler
+            // then keeps them in scalar registers)
+            segment(__builtin_amdgcn_readfirstlane(lo), 0, __builtin_amdgcn_readfirstlane(e - g),
+                    __builtin_amdgcn_readfirstlane((g == p0 && e == p1) ? -1 : lo + blk));
             g = e;
         }
         return;
