@@ -22,7 +22,8 @@
 //    max / sum live in one lane pair (one permlane32 swap) and rescaling the
 //    output is a per-lane multiply.
 //  * O^T += V^T P^T: P comes straight from the S^T accumulator layout
-//    (exp2 of S * scale*log2(e) - m, rounded to bf16); V^T operands are read
+//    (exp2 of S - m, rounded to bf16, with S in base-2 units because the
+//    Q fragments carry scale*log2(e)); V^T operands are read
 //    with ds_read_b64_tr_b16, whose 16-lane 4x16 -> 16x4 transpose turns the
 //    row-major V tile into the key-contiguous operand, in the key order that
 //    matches P.
@@ -58,17 +59,24 @@ static constexpr int kStages = 4;         // LDS ring depth (tiles)
 static constexpr int kTileElems = kBN * kD;
 static constexpr int kRowsPerWave = kBN / kWaves;   // tile rows each wavefront copies
 static constexpr int kCopies = kRowsPerWave / 4;    // 1 KB copies per tensor per wavefront
-// The probabilities of a sub-tile are taken against a reference max m that
-// only moves when a row's new probabilities sum past 2^8 (some score more than
-// 2^4 above m, or an overflow): O and l are then rescaled and the sub-tile's
-// probabilities recomputed.  The result is exact either way, since O and l
-// always share the reference max, and no per-sub-tile maximum is needed.
+// Scores are kept in base-2 units: the Q fragments carry the factor
+// c = softmax_scale * log2(e) (one bf16 rounding of q * c), so p = 2^(s - m).
+// The probabilities of a sub-tile are taken against a reference max m (the
+// row max of the segment's first sub-tile) that only moves when a row's new
+// probabilities sum past 2^8 (some score more than 8 above m, or an
+// overflow): O and l are then rescaled and the sub-tile's probabilities
+// recomputed.  The result is exact either way, since O and l always share the
+// reference max, and no per-sub-tile maximum is needed.  Every chain of score
+// products starts from the accumulator value -m, so the scores arrive already
+// shifted and the exponentials take them as they are (no vector operation
+// per score before the exponential).
 static constexpr float kSumLimit = 256.f;
 // LDS operands are read this many matrix products ahead of their use (of the
-// 8 per region); 2, 4, 5, 6, 7 and 8 measured 1.38, 1.37, 1.36, 1.36, 1.41
-// and 1.40 ms on the Wan-shaped launch: 6 hides the LDS latency best within
-// the register budget.
-static constexpr int kPrefetch = 6;
+// 8 per region).  With the -m start vector (16 registers) live, 3 is the
+// deepest that fits 256 registers without spills in every mode: on the
+// Wan-shaped launch 3 measured 1.311 ms and 5 (with spills) 1.306 ms; before
+// the start vector, 2 and 6 measured 1.420 and 1.367 ms.
+static constexpr int kPrefetch = 3;
 static constexpr int kMaxSplitBlocks = 256;  // blocks of a split launch (partial slots)
 static constexpr int kMinSplitTiles = 16;    // fewest tiles per block worth a split
 static constexpr int kMaxBlocksPerItem = 32; // split blocks per (query block, head) item
@@ -99,7 +107,7 @@ struct AttnArgs {
     void *out;
     float *lse;
     float *part_o;      // [items][slots][kBM][kD] unnormalised partial outputs
-    float *part_ml;     // [items][slots][kBM][2] reference max and row sum
+    float *part_ml;     // [items][slots][kBM][2] reference max (base-2 units), row sum
     // paged context (idx != null): k_ctx / v_ctx are the pools, context key n
     // is token n % page_tokens of pool page idx[n / page_tokens]
     const int32_t *idx;
@@ -413,15 +421,20 @@ void k_attn_bf16(AttnArgs a) {
         dma16<OV + ROWS4>(vr[1], ld_base);
     };
 
-    // ---- this wavefront's 32 queries as B operands: qf[st] = Q[q0+lr][16st+8hb ..+7]
+    // ---- this wavefront's 32 queries as B operands, in base-2 score units:
+    // qf[st] = bf16(c * Q[q0+lr][16st+8hb ..+7])
     bf16x8 qf[8];
     {
         const int row = q0 + lr;
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            if (row < a.n_q)
-                qf[st] = *(const bf16x8 *)(a.q + (int64_t)row * hd + h * kD + 16 * st + 8 * hb);
-            else
+            if (row < a.n_q) {
+                const bf16x8 raw = *(const bf16x8 *)(a.q + (int64_t)row * hd + h * kD + 16 * st + 8 * hb);
+                bf16x8 scaled;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) scaled[e] = (__bf16)((float)raw[e] * c);
+                qf[st] = scaled;
+            } else
                 qf[st] = (bf16x8)(__bf16)0.f;
         }
     }
@@ -431,7 +444,8 @@ void k_attn_bf16(AttnArgs a) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
-    float m = -3.0e38f, l = 0.f;   // finite: no inf - inf anywhere
+    float m = 0.f, l = 0.f;   // reference max (base-2 units), row sum
+    f32x16 cinit;             // -m in every element: start of each score chain
 
     // ---- keys past the end (last tile only) get score -inf.  Their rows were
     // loaded as copies of the last key, so maxima taken before masking are
@@ -446,7 +460,7 @@ void k_attn_bf16(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
             if (8 * (i >> 2) + (i & 3) >= lim) s[i] = -INFINITY;
     };
-    // ---- region QK+SOFTMAX: sn = K Q^T of the sub-tile at koff (8 MFMAs)
+    // ---- region QK+SOFTMAX: sn = K Q^T - m of the sub-tile at koff (8 MFMAs)
     // interleaved with the exponentials of sc (2 elements per MFMA), P packed to
     // bf16 for the P V products, l accumulated from the bf16 values; then the
     // lazy-rescale test (see kSumLimit).  Operands are read kPf products
@@ -455,15 +469,13 @@ void k_attn_bf16(AttnArgs a) {
     // products of this one.
     auto qk_softmax = [&](int koff, f32x16 &sn, const f32x16 &sc, bf16x8 (&pb)[2],
                           bf16x8 (&ak)[8], int voff, bf16x8 (&av)[8]) __attribute__((always_inline)) {
-        const float mc = m * c;
         float ls0 = 0.f, ls1 = 0.f;
-        const f32x16 zero = {};
         const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sn, 0, 0, 0);
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st], c, -mc));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st + 1], c, -mc));
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? cinit : sn, 0, 0, 0);
+            const float p0 = __builtin_amdgcn_exp2f(sc[2 * st]);
+            const float p1 = __builtin_amdgcn_exp2f(sc[2 * st + 1]);
             const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
             pb[st >> 2][2 * (st & 3)] = pr[0];
             pb[st >> 2][2 * (st & 3) + 1] = pr[1];
@@ -478,20 +490,26 @@ void k_attn_bf16(AttnArgs a) {
             float x = fmaxf(sc[0], sc[1]);
 #pragma unroll
             for (int i = 1; i < 8; ++i) x = fmaxf(x, fmaxf(sc[2 * i], sc[2 * i + 1]));
-            const float mn = fmaxf(m, xhalf_max(x));
-            const float corr = __builtin_amdgcn_exp2f((m - mn) * c);
+            // the new reference max is m + dm; sn, already started from -m,
+            // is moved to it as well
+            const float dm = fmaxf(xhalf_max(x), 0.f);
+            const float corr = __builtin_amdgcn_exp2f(-dm);
             l *= corr;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[b][i] *= corr;
-            m = mn;
-            const float mc2 = m * c;
+            m += dm;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                cinit[i] = -m;
+                sn[i] -= dm;
+            }
             lsub = 0.f;
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st], c, -mc2));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * st + 1], c, -mc2));
+                const float p0 = __builtin_amdgcn_exp2f(sc[2 * st] - dm);
+                const float p1 = __builtin_amdgcn_exp2f(sc[2 * st + 1] - dm);
                 const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
                 pb[st >> 2][2 * (st & 3)] = pr[0];
                 pb[st >> 2][2 * (st & 3) + 1] = pr[1];
@@ -549,12 +567,23 @@ void k_attn_bf16(AttnArgs a) {
         for (int st = 0; st < 8; ++st)
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sa, 0, 0, 0);
         if (t_begin == mask_tile) mask_tail(sa, mask_key0);
+        // its row max is the first reference max (a masked sub-tile still
+        // holds at least one real key: the last tile's first key)
+        float x = fmaxf(sa[0], sa[1]);
+#pragma unroll
+        for (int i = 1; i < 8; ++i) x = fmaxf(x, fmaxf(sa[2 * i], sa[2 * i + 1]));
+        m = xhalf_max(x);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sa[i] -= m;
+            cinit[i] = -m;
+        }
 #pragma unroll
         for (int st = 0; st < kPf; ++st) ak[st] = read_k(kSubBytes, st);
     }
 
-    // Tile t in stage S; on entry sa = S(t, 0) with the reference max already
-    // moved, and the first two K operands of S(t, 1) prefetched.  Stages S+1
+    // Tile t in stage S; on entry sa = S(t, 0) - m, and the first kPf K
+    // operands of S(t, 1) prefetched.  Stages S+1
     // and S+2 hold (or are receiving) tiles t+1 and t+2; stage S+3 is refilled
     // with tile min(t+3, last).  On exit sa = S(t+1, 0), likewise.  The last
     // tile runs the same code: its products of the (nonexistent) next tile
@@ -623,7 +652,7 @@ void k_attn_bf16(AttnArgs a) {
                 }
             }
         if (a.lse && hb == 0)
-            a.lse[(int64_t)h * a.n_q + row] = (m * c + __log2f(lt)) * 0.69314718055994531f;
+            a.lse[(int64_t)h * a.n_q + row] = (m + __log2f(lt)) * 0.69314718055994531f;
     }
   };
 
@@ -747,7 +776,6 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     const int row = qb * kBM + r;
     if (row >= a.n_q) return;
     const int64_t hd = (int64_t)a.n_heads * kD;
-    const float c = a.c;
     const int d = 4 * (threadIdx.x & 31);
     const int64_t row0 = SPARSE ? (int64_t)first_slot * kBM + r : (int64_t)item * a.slots * kBM + r;
     float M = -INFINITY, L = 0.f;
@@ -757,8 +785,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         const float2 ml = *(const float2 *)(a.part_ml + 2 * pr);
         const float4 v = *(const float4 *)(a.part_o + pr * kD + d);
         const float mn = fmaxf(M, ml.x);
-        const float fo = __builtin_amdgcn_exp2f((M - mn) * c);   // 0 on the first piece
-        const float f = __builtin_amdgcn_exp2f((ml.x - mn) * c);
+        const float fo = __builtin_amdgcn_exp2f(M - mn);   // 0 on the first piece
+        const float f = __builtin_amdgcn_exp2f(ml.x - mn);
         L = L * fo + ml.y * f;
         acc.x = acc.x * fo + v.x * f;
         acc.y = acc.y * fo + v.y * f;
@@ -778,7 +806,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (a.lse && d == 0)
-        a.lse[(int64_t)h * a.n_q + row] = (M * c + __log2f(L)) * 0.69314718055994531f;
+        a.lse[(int64_t)h * a.n_q + row] = (M + __log2f(L)) * 0.69314718055994531f;
 }
 
 // Plan of a sparse launch, from the item counts on the device (the host never

@@ -104,7 +104,19 @@ def test_attention_scores_growing_along_the_keys(wl):
     ref, ref_lse = oracle.attention(q, kc, vc, ko, vo, wl.softmax_scale)
     tol = 1e-5 if wl.dtype == W.F32 else 1e-2
     assert np.abs(to_f64(out) - ref).max() <= tol
-    assert np.abs(lse.cpu().double().numpy() - ref_lse).max() <= tol
+    lse_tol = tol
+    if wl.dtype != W.F32:
+        # the bf16 kernel multiplies q by scale * log2(e) and rounds the
+        # product to bf16 (relative error <= 2^-8 per element) before the
+        # score products, so score n of query i moves by at most
+        # 2^-8 * scale * sum_d |q_id k_nd| (natural units), and the
+        # log-sum-exp by at most the largest such move; these scores reach
+        # about 17, far beyond unit-variance data
+        qa = np.abs(W.bf16_bits_to_f32(q).astype(np.float64))
+        ka = np.abs(W.bf16_bits_to_f32(np.concatenate([kc, ko])).astype(np.float64))
+        move = 2.0 ** -8 * wl.softmax_scale * np.einsum("ihd,nhd->hin", qa, ka).max(axis=2)
+        lse_tol = tol + move
+    assert (np.abs(lse.cpu().double().numpy() - ref_lse) <= lse_tol).all()
 
 
 def test_attention_unit_values_and_reruns_are_bitwise_equal():
