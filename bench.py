@@ -319,6 +319,17 @@ def sparse_pass(wa, W, wl, L, up, k_ctx, v_ctx, k_own, v_own, out, stream, steps
     torch.cuda.synchronize()
     sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # a chunk's later denoising steps: same context, so the selection takes
+    # the context block sums the calls above left in ws
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(steps):
+        rev[k][0].record(stream)
+        wa.wa_hsa_select(L, q_sp, k_ctx, k_own, tau, scale=wl.softmax_scale, sel_tiles=tiles,
+                         sel_count=count, want_gini=False, workspace=ws, ctx_sums_ready=True,
+                         stream=stream)
+        rev[k][1].record(stream)
+    torch.cuda.synchronize()
+    sel_reuse_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in rev]))
     # flops over the keys actually attended: per item, its query rows times
     # the keys of its listed tiles (the last tile of [ctx ++ own] is short)
     t_h, c_h = tiles.cpu().numpy(), count.cpu().numpy()
@@ -341,6 +352,8 @@ def sparse_pass(wa, W, wl, L, up, k_ctx, v_ctx, k_own, v_own, out, stream, steps
         "attention_TFLOP/s_on_kept_keys": round(tflops, 2),
         "attention_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "speedup_vs_dense_attention": round(dense_ms / (sel_ms + att_ms), 3),
+        "select_ms_context_sums_reused": round(sel_reuse_ms, 4),
+        "speedup_vs_dense_attention_later_steps": round(dense_ms / (sel_reuse_ms + att_ms), 3),
     }
 
 

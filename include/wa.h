@@ -330,8 +330,16 @@ size_t wa_hsa_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ct
  * V is not read).  tau: device [H] double.  sel_tiles: device int32
  * [q_blocks * H][n_tiles]; sel_count: device int32 [q_blocks * H]; gini:
  * device double [q_blocks * H] or NULL.  scale: the score scale (the
- * attention's softmax_scale).  workspace: device, >= wa_hsa_workspace_bytes
- * bytes, 16-byte aligned; calls in flight at once need separate workspaces.
+ * attention's softmax_scale).  ctx_sums_ready: 0 pools every block;
+ * nonzero takes the context key blocks' sums already in the workspace as
+ * they are (the own and query blocks are always pooled): they must have been
+ * left there by an earlier call with this workspace, the same layout and
+ * n_ctx, and the same k_ctx contents.  The context does not change over a
+ * chunk's denoising steps (Inferix summary, section 3.4, Step 3), so the
+ * chunk's first step pools it and the later steps reuse it.  The library
+ * cannot check this; other sums give other selections.  workspace: device,
+ * >= wa_hsa_workspace_bytes bytes, 16-byte aligned; calls in flight at once
+ * need separate workspaces.
  * Errors: NULL layout / q / tau / sel_tiles / sel_count / workspace, NULL
  * pointer of a non-empty segment, n_q < 1, n_ctx < 0, n_own < 0,
  * n_ctx + n_own < 1, scale not finite and > 0, misaligned pointers,
@@ -342,7 +350,7 @@ size_t wa_hsa_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ct
 wa_status wa_hsa_select(const wa_layout *layout, const void *q, int32_t n_q, const void *k_ctx,
                         int32_t n_ctx, const void *k_own, int32_t n_own, double scale,
                         const double *tau, int32_t *sel_tiles, int32_t *sel_count, double *gini,
-                        void *workspace, size_t ws_bytes, void *stream);
+                        int32_t ctx_sums_ready, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Sparse branch, attention over the selected blocks (WorldAttention review,

@@ -109,7 +109,8 @@ def load_library():
     lib.wa_paged_attention.restype = i32
     lib.wa_hsa_workspace_bytes.argtypes = [L, i32, i32, i32]
     lib.wa_hsa_workspace_bytes.restype = sz
-    lib.wa_hsa_select.argtypes = [L, p, i32, p, i32, p, i32, ctypes.c_double, p, p, p, p, p, sz, p]
+    lib.wa_hsa_select.argtypes = [L, p, i32, p, i32, p, i32, ctypes.c_double, p, p, p, p, i32, p,
+                                  sz, p]
     lib.wa_hsa_select.restype = i32
     lib.wa_sparse_attention.argtypes = [L, p, i32, p, p, i32, p, p, i32, f32, p, p, i32, p, p, p,
                                         sz, p]
@@ -431,10 +432,14 @@ def wa_hsa_workspace_bytes(L: Layout, n_q: int, n_ctx: int, n_own: int) -> int:
 
 
 def wa_hsa_select(L: Layout, q, k_ctx, k_own, tau, scale=None, sel_tiles=None, sel_count=None,
-                  gini=None, want_gini=True, workspace=None, stream=None):
+                  gini=None, want_gini=True, workspace=None, ctx_sums_ready=False, stream=None):
     """Block selection of the sparse branch; returns (sel_tiles [items,
     n_tiles] int32, sel_count [items] int32, gini [items] float64 or None).
-    tau: device float64 [H]."""
+    tau: device float64 [H].  ctx_sums_ready: reuse the context block sums an
+    earlier call left in `workspace` (same layout, n_ctx and k_ctx contents);
+    it needs that workspace passed in."""
+    if ctx_sums_ready and workspace is None:
+        raise ValueError("wa_hsa_select: ctx_sums_ready needs the workspace of the earlier call")
     lib = load_library()
     dt, row = L.torch_dtype, L.row_elems
     _need(q, "q", dt)
@@ -458,7 +463,8 @@ def wa_hsa_select(L: Layout, q, k_ctx, k_own, tau, scale=None, sel_tiles=None, s
     ws = _workspace(nbytes, workspace, q)
     st = lib.wa_hsa_select(ctypes.byref(L), _ptr(q), int(n_q), _ptr(k_ctx), int(n_ctx),
                            _ptr(k_own), int(n_own), float(scale), _ptr(tau), _ptr(sel_tiles),
-                           _ptr(sel_count), _ptr(gini), _ptr(ws), ws.numel(), _stream(stream))
+                           _ptr(sel_count), _ptr(gini), 1 if ctx_sums_ready else 0, _ptr(ws),
+                           ws.numel(), _stream(stream))
     _check(st, "wa_hsa_select")
     return sel_tiles, sel_count, gini
 

@@ -61,15 +61,17 @@ size_t hsa_workspace_bytes(int64_t hd, const HsaShape &w) {
            (size_t)w.items * (w.nb_ctx + w.nb_own) * sizeof(double);
 }
 
-// blockIdx.x: column group; blockIdx.y: a context key block, an own key block
-// or a query block, in that order.  Each writes the column sums of its rows.
+// blockIdx.x: column group; blockIdx.y + y0: a context key block, an own key
+// block or a query block, in that order (y0 = nb_ctx skips the context
+// blocks, whose sums an earlier call left in place).  Each writes the column
+// sums of its rows.
 template <bool BF16>
 __global__ __launch_bounds__(kHsaThreads) void k_hsa_pool(
     const uint4 *__restrict__ k_ctx, int n_ctx, const uint4 *__restrict__ k_own, int n_own,
     const uint4 *__restrict__ q, int n_q, int nb_ctx, int nb_own, int chunks, int group_chunks,
-    int hd, double *__restrict__ ksum, double *__restrict__ qsum) {
+    int hd, int y0, double *__restrict__ ksum, double *__restrict__ qsum) {
     __shared__ double lds[kHsaRowLanes * 64 * (BF16 ? 8 : 4)];
-    int y = blockIdx.y;
+    int y = blockIdx.y + y0;
     const uint4 *x;
     int rows, per_block;
     double *out;
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(kHsaThreads) void k_hsa_select(
 hipError_t launch_hsa_select(const wa_layout &L, const void *q, int32_t n_q, const void *k_ctx,
                              int32_t n_ctx, const void *k_own, int32_t n_own, double scale,
                              const double *tau, int32_t *tiles, int32_t *count, double *gini,
-                             void *ws, hipStream_t s) {
+                             bool ctx_sums_ready, void *ws, hipStream_t s) {
     const int64_t hd = (int64_t)L.n_heads * L.head_dim;
     const HsaShape w = hsa_shape(L.n_heads, n_q, n_ctx, n_own);
     double *ksum = (double *)ws;
@@ -373,15 +375,16 @@ hipError_t launch_hsa_select(const wa_layout &L, const void *q, int32_t n_q, con
     const int chunks = (int)(hd / vec);
     const int group_chunks = chunks < 64 ? chunks : 64;
     const int groups = (chunks + group_chunks - 1) / group_chunks;
-    const dim3 grid((unsigned)groups, (unsigned)(w.nb_ctx + w.nb_own + w.q_blocks));
+    const int y0 = ctx_sums_ready ? w.nb_ctx : 0;
+    const dim3 grid((unsigned)groups, (unsigned)(w.nb_ctx + w.nb_own + w.q_blocks - y0));
     if (L.dtype == WA_BF16)
         hipLaunchKernelGGL(k_hsa_pool<true>, grid, dim3(kHsaThreads), 0, s, (const uint4 *)k_ctx,
                            n_ctx, (const uint4 *)k_own, n_own, (const uint4 *)q, n_q, w.nb_ctx,
-                           w.nb_own, chunks, group_chunks, (int)hd, ksum, qsum);
+                           w.nb_own, chunks, group_chunks, (int)hd, y0, ksum, qsum);
     else
         hipLaunchKernelGGL(k_hsa_pool<false>, grid, dim3(kHsaThreads), 0, s, (const uint4 *)k_ctx,
                            n_ctx, (const uint4 *)k_own, n_own, (const uint4 *)q, n_q, w.nb_ctx,
-                           w.nb_own, chunks, group_chunks, (int)hd, ksum, qsum);
+                           w.nb_own, chunks, group_chunks, (int)hd, y0, ksum, qsum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nb = w.nb_ctx + w.nb_own;

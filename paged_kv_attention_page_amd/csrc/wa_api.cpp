@@ -250,7 +250,7 @@ size_t wa_hsa_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_ctx, in
 wa_status wa_hsa_select(const wa_layout *L, const void *q, int32_t n_q, const void *k_ctx,
                         int32_t n_ctx, const void *k_own, int32_t n_own, double scale,
                         const double *tau, int32_t *sel_tiles, int32_t *sel_count, double *gini,
-                        void *workspace, size_t ws_bytes, void *stream) {
+                        int32_t ctx_sums_ready, void *workspace, size_t ws_bytes, void *stream) {
     const wa_status st = check_layout(L, false);
     if (st != WA_OK) return st;
     if (!q || !tau || !sel_tiles || !sel_count || !workspace) return WA_ERR_INVALID_ARG;
@@ -268,7 +268,8 @@ wa_status wa_hsa_select(const wa_layout *L, const void *q, int32_t n_q, const vo
     if (ws_bytes < hsa_workspace_bytes((int64_t)L->n_heads * L->head_dim, w))
         return WA_ERR_INVALID_ARG;
     return from_hip(launch_hsa_select(*L, q, n_q, k_ctx, n_ctx, k_own, n_own, scale, tau,
-                                      sel_tiles, sel_count, gini, workspace, (hipStream_t)stream));
+                                      sel_tiles, sel_count, gini, ctx_sums_ready != 0 && n_ctx > 0,
+                                      workspace, (hipStream_t)stream));
 }
 
 size_t wa_sparse_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_ctx,

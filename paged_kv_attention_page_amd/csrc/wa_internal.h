@@ -145,6 +145,6 @@ size_t hsa_workspace_bytes(int64_t hd, const HsaShape &w);
 hipError_t launch_hsa_select(const wa_layout &L, const void *q, int32_t n_q, const void *k_ctx,
                              int32_t n_ctx, const void *k_own, int32_t n_own, double scale,
                              const double *tau, int32_t *tiles, int32_t *count, double *gini,
-                             void *ws, hipStream_t s);
+                             bool ctx_sums_ready, void *ws, hipStream_t s);
 
 }  // namespace wa

@@ -321,13 +321,13 @@ def test_hsa_workspace_size(lib):
 def _hsel(lib, lay=None, q=A, n_q=300, kc=A, n_ctx=640, ko=B, n_own=100, scale=0.1, tau=A,
           tiles=B, count=A, gini=NULL, ws=A, ws_bytes=1 << 20):
     return lib.wa_hsa_select(lay if lay is not None else L(), q, n_q, kc, n_ctx, ko, n_own, scale,
-                             tau, tiles, count, gini, ws, ws_bytes, None)
+                             tau, tiles, count, gini, 0, ws, ws_bytes, None)
 
 
 def test_hsa_select_rejects(lib):
     """Every argument rule of wa_hsa_select, one bad argument per call."""
     E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
-    assert lib.wa_hsa_select(None, A, 300, A, 640, B, 100, 0.1, A, B, A, NULL, A, 1 << 20,
+    assert lib.wa_hsa_select(None, A, 300, A, 640, B, 100, 0.1, A, B, A, NULL, 0, A, 1 << 20,
                              None) == E
     for bad in ("q", "tau", "tiles", "count", "ws"):
         assert _hsel(lib, **{bad: NULL}) == E, bad

@@ -123,6 +123,48 @@ def test_selection_one_segment_only():
     _check_selection(L, wl, q, None, ko, [0.6, 0.85, 0.4], wl.softmax_scale)
 
 
+def test_selection_reusing_the_context_sums():
+    """Two denoising steps of one chunk: the context keys stay, the queries and
+    own keys are drawn anew.  The second call takes the context block sums the
+    first left in the workspace (ctx_sums_ready) and must equal, bit for bit,
+    a call that pools every block, which is held to the oracle."""
+    wl = SMALL
+    L = wa_layout(wl)
+    n_ctx, n_own = 576, 560
+    q1, kc, _, ko1, _ = _inputs(wl, [5, 0, 3, 7, 2], n_ctx, n_own, gain=8.0)
+    q2 = W.aligned_queries(wl, 0, 1, 6.0)
+    _, ko2, _ = W.chunk_qkv(wl, 0, 1)
+    ko2 = ko2[:n_own]
+    tau = [0.5, 0.8, 0.95]
+    tau_d = torch.tensor(tau, dtype=torch.float64, device="cuda")
+    kcd = to_device(kc)
+    ws = torch.empty(wa.wa_hsa_workspace_bytes(L, q1.shape[0], n_ctx, n_own), dtype=torch.uint8,
+                     device="cuda")
+    say("hsa select, step 1 pools everything")
+    wa.wa_hsa_select(L, to_device(q1), kcd, to_device(ko1), tau_d, scale=wl.softmax_scale,
+                     workspace=ws)
+    say("hsa select, step 2 reuses the context sums")
+    reused = wa.wa_hsa_select(L, to_device(q2), kcd, to_device(ko2), tau_d,
+                              scale=wl.softmax_scale, workspace=ws, ctx_sums_ready=True)
+    torch.cuda.synchronize()
+    reused = [x.cpu().numpy() for x in reused]
+    full_tiles, full_count = _check_selection(L, wl, q2, kc, ko2, tau, wl.softmax_scale)
+    fresh = wa.wa_hsa_select(L, to_device(q2), kcd, to_device(ko2), tau_d,
+                             scale=wl.softmax_scale)
+    torch.cuda.synchronize()
+    fresh = [x.cpu().numpy() for x in fresh]
+    # counts and Gini coefficients bit for bit; each list up to its count (the
+    # entries after it are not written)
+    assert np.array_equal(reused[1], fresh[1]) and np.array_equal(reused[1], full_count)
+    assert np.array_equal(reused[2].view(np.int64), fresh[2].view(np.int64))
+    for item in range(reused[1].size):
+        c = reused[1][item]
+        assert np.array_equal(reused[0][item, :c], fresh[0][item, :c])
+        assert np.array_equal(reused[0][item, :c], full_tiles[item, :c])
+    with pytest.raises(ValueError):
+        wa.wa_hsa_select(L, to_device(q2), kcd, to_device(ko2), tau_d, ctx_sums_ready=True)
+
+
 def _sparse_vs_oracle(wl, q, kc, vc, ko, vo, tau, rows=None, out_dtypes=(wa.WA_F32, wa.WA_BF16)):
     L = wa_layout(wl)
     tiles, count = _check_selection(L, wl, q, kc, ko, tau, wl.softmax_scale)
