@@ -36,6 +36,13 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 
 
+def cold_entry(ms, nbytes):
+    """An HBM kernel's figures after a 1 GiB overwrite (L2s and MALL evicted)."""
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "note": "median of 10 reps, each after a 1 GiB overwrite (L2 and MALL evicted)"}
+
+
 def attention_flops(n_q, n_k, head_dim, n_heads):
     """2 FLOP per multiply-add, two contractions (Q K^T and P V); softmax excluded."""
     return 4.0 * n_q * n_k * head_dim * n_heads
@@ -54,6 +61,67 @@ def parse():
                                                       "k_attn_bf16_wan_kp4_hbm_traffic.txt"),
                     help="HBM traffic summary from rocprofv3 counters (optional)")
     return ap.parse_args()
+
+
+class ClockSampler:
+    """GFX clock and socket power of the GPU (amdsmi GPU metrics, every 10 ms:
+    the firmware's averaged GFX clock, the current clock of each XCD, the
+    memory clock) while the timed steps run.  Everything happens on a daemon thread, so a monitoring library
+    that is missing or refuses never stalls or fails the bench; the summary
+    then names the reason instead of the clocks."""
+
+    def __init__(self, pci_bus_id):
+        import threading
+        self.bus = pci_bus_id
+        self.gfx, self.xcd, self.mem, self.power = [], [], [], []
+        self.error = None
+        self.stop_flag = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) > 1 and self.bus is not None:
+                handles = [h for h in handles
+                           if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == self.bus]
+            if len(handles) != 1:
+                raise RuntimeError("%d matching GPUs" % len(handles))
+            h = handles[0]
+            num = lambda x: isinstance(x, (int, float))
+            while not self.stop_flag.is_set():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                self.gfx.append(m.get("average_gfxclk_frequency"))
+                xcd = [x for x in (m.get("current_gfxclks") or []) if num(x) and x > 0]
+                if xcd:
+                    self.xcd.append(float(np.mean(xcd)))
+                mem = m.get("average_uclk_frequency", m.get("current_uclk"))
+                if not num(mem):
+                    mem = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"]
+                self.mem.append(mem)
+                self.power.append(m.get("average_socket_power", m.get("current_socket_power")))
+                self.stop_flag.wait(0.01)
+        except Exception as e:          # report, never fail the bench
+            self.error = "%s: %s" % (type(e).__name__, e)
+
+    def start(self):
+        self.thread.start()
+
+    def stop(self):
+        self.stop_flag.set()
+        self.thread.join(timeout=2.0)
+        def stats(v):
+            v = [x for x in v if isinstance(x, (int, float))]
+            if not v:
+                return None
+            return {"median": float(np.median(v)), "min": float(min(v)), "max": float(max(v))}
+        if self.error or not self.gfx:
+            return {"note": "not sampled (%s)" % (self.error or "no samples")}
+        return {"unit": "MHz (power: W)", "samples": len(self.gfx),
+                "gfx_average": stats(self.gfx), "gfx_current_xcd_mean": stats(self.xcd),
+                "mem": stats(self.mem), "socket_power": stats(self.power),
+                "note": "amdsmi GPU metrics every 10 ms over the timed steps"}
 
 
 def main():
@@ -147,12 +215,15 @@ def main():
     # K timed steps between two synchronisations; HIP events recorded on the
     # launch stream inside the same region give the per-kernel durations
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    clocks = ClockSampler(getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None))
+    clocks.start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock_summary = clocks.stop()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     names = ("append", "select_gather", "attention")
@@ -168,6 +239,29 @@ def main():
     torch.cuda.synchronize()
     split = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sev]))
              for i, n in enumerate(("select", "gather"))}
+
+    # cold pass (after the timed region): a 1 GiB overwrite before each rep
+    # evicts the L2s and the 256 MB MALL, so the HBM kernels start from HBM;
+    # the in-step figures above run with the step's other kernels in between
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = {"append": [], "select_gather": []}
+    for k in range(10):
+        for name in ("append", "select_gather"):
+            flush.fill_(k & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if name == "append":
+                wa.wa_append_page(L, k_new, v_new, k_pool, v_pool, spare, means,
+                                  workspace=ws_append, stream=stream)
+            else:
+                wa.wa_select_pages(L, q, means, wl.k_p, cand=cand, out_idx=idx, workspace=ws_sel,
+                                   stream=stream)
+                wa.wa_gather(L, k_pool, v_pool, idx, wl.k_p, k_ctx, v_ctx, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold[name].append(e0.elapsed_time(e1))
+    del flush
+    cold_ms = {n: float(np.median(v)) for n, v in cold.items()}
 
     # paged pass (after the timed region; not part of the step figure): the
     # same step with the attention reading the selected pages in place from
@@ -257,11 +351,14 @@ def main():
             "split_pass_ms": {k: round(v, 4) for k, v in split.items()},
             "gather_GB/s": round(bytes_gather / (split["gather"] * 1e-3) / 1e9, 1),
             "select_GB/s": round(bytes_select / (split["select"] * 1e-3) / 1e9, 1),
+            "cold": cold_entry(cold_ms["select_gather"], bytes_select + bytes_gather),
         },
         "append": {
             "bytes": bytes_append,
             "GB/s": round(bytes_append / (avg["append"] * 1e-3) / 1e9, 1),
+            "cold": cold_entry(cold_ms["append"], bytes_append),
         },
+        "clocks": clock_summary,
         "paged": {
             "note": "append + select + wa_paged_attention (pages read in place, no gather), "
                     "same inputs, timed after the step figure",
