@@ -344,6 +344,7 @@ def main():
         },
         "kernels_ms": {k: round(v, 4) for k, v in avg.items()},
         "kernels_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "kernels_ms_min": {k: round(float(np.min(v)), 4) for k, v in per.items()},
         "select_gather": {
             "bytes": bytes_select + bytes_gather,
             "GB/s": round(sg_gbps, 1),
@@ -374,7 +375,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h,
+        result["cpu_baseline"] = cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means,
                                               args.cpu_seconds, torch)
     print(json.dumps(result), flush=True)
 
@@ -543,9 +544,21 @@ def load_traffic(path, kernel_src):
     return int(fields["bytes_per_launch"])
 
 
-def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, seconds, torch):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch):
     """The fp64 oracle's attention on a bounded sample of query rows (all heads),
-    on the host cores, in the metric's unit (TFLOP/s)."""
+    on the host cores, in the metric's unit (TFLOP/s); the other stages of the
+    step (one page mean, the selection, the gather) timed once each beside it."""
     import oracle
     oracle.build(force=False)
     sel = idx.cpu().numpy()
@@ -567,6 +580,21 @@ def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, seconds, torch):
                          threads=threads)
         dt = time.perf_counter() - t0
     fl = attention_flops(len(rows), n_k, wl.head_dim, wl.n_heads)
+    stages = {}
+    t0 = time.perf_counter()
+    oracle.page_mean(k_ctx[:wl.page_tokens])
+    stages["append_page_mean"] = time.perf_counter() - t0
+    pm = np.ascontiguousarray(means[:wl.n_pages].cpu().numpy())
+    t0 = time.perf_counter()
+    oracle.select_pages(q_h, pm, wl.k_p)
+    stages["select"] = time.perf_counter() - t0
+    pages = np.ascontiguousarray(k_ctx.reshape(wl.k_p, wl.page_tokens, wl.n_heads, wl.head_dim))
+    pages_v = np.ascontiguousarray(v_ctx.reshape(wl.k_p, wl.page_tokens, wl.n_heads, wl.head_dim))
+    order = np.arange(wl.k_p, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.gather(pages, order)
+    oracle.gather(pages_v, order)
+    stages["gather"] = time.perf_counter() - t0
     return {
         "value": round(fl / dt / 1e12, 6),
         "unit": "TFLOP/s",
@@ -574,6 +602,13 @@ def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, seconds, torch):
         "kind": "oracle",
         "sample": "block attention of %d of %d query rows x %d heads over %d keys (fp64, "
                   "%.1f s)" % (len(rows), wl.n_q, wl.n_heads, n_k, dt),
+        "stages_s": {k: round(v, 4) for k, v in stages.items()},
+        "stages_note": "the oracle once each: the mean key of one page, the selection over "
+                       "the %d resident pages (mean query, scores, top-%d), the gather of the "
+                       "K and V of %d pages (single-threaded; attention uses the cores above)"
+                       % (wl.n_pages, wl.k_p, wl.k_p),
+        "nproc": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
 
 
