@@ -163,6 +163,17 @@ def test_selection_reusing_the_context_sums():
         assert np.array_equal(reused[0][item, :c], full_tiles[item, :c])
     with pytest.raises(ValueError):
         wa.wa_hsa_select(L, to_device(q2), kcd, to_device(ko2), tau_d, ctx_sums_ready=True)
+    # no context keys: the flag has nothing to reuse and is ignored
+    say("hsa select, own keys only, flag set")
+    own_only = wa.wa_hsa_select(L, to_device(q2), None, to_device(ko2), tau_d,
+                                scale=wl.softmax_scale, workspace=ws, ctx_sums_ready=True)
+    plain = wa.wa_hsa_select(L, to_device(q2), None, to_device(ko2), tau_d, scale=wl.softmax_scale)
+    torch.cuda.synchronize()
+    a_t, a_c, a_g = [x.cpu().numpy() for x in own_only]
+    b_t, b_c, b_g = [x.cpu().numpy() for x in plain]
+    assert np.array_equal(a_c, b_c) and np.array_equal(a_g.view(np.int64), b_g.view(np.int64))
+    for item in range(a_c.size):
+        assert np.array_equal(a_t[item, :a_c[item]], b_t[item, :b_c[item]])
 
 
 def _sparse_vs_oracle(wl, q, kc, vc, ko, vo, tau, rows=None, out_dtypes=(wa.WA_F32, wa.WA_BF16)):
