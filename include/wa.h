@@ -337,7 +337,8 @@ size_t wa_hsa_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_ct
  * n_ctx, and the same k_ctx contents.  The context does not change over a
  * chunk's denoising steps (Inferix summary, section 3.4, Step 3), so the
  * chunk's first step pools it and the later steps reuse it.  The library
- * cannot check this; other sums give other selections.  workspace: device,
+ * cannot check this; other sums give other selections.  With n_ctx = 0 the
+ * flag is ignored.  workspace: device,
  * >= wa_hsa_workspace_bytes bytes, 16-byte aligned; calls in flight at once
  * need separate workspaces.
  * Errors: NULL layout / q / tau / sel_tiles / sel_count / workspace, NULL
