@@ -51,6 +51,12 @@ def attention_flops(n_q, n_k, head_dim, n_heads):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--config", default="2", choices=["2", "3", "5", "share"],
+                    help="2: the Wan-shaped K_p=4 step (the headline line); 3: full history "
+                         "(6 pages, all attended, 4 denoising steps per chunk); 5: long horizon "
+                         "(128 -> 136 resident pages, 8 chunks x 4 steps, one page appended per "
+                         "chunk); share: config 2 at 3 heads, one GPU's share of a 4-way "
+                         "head-sharded layer")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30,
                     help="untimed steps first; the clock takes ~20 launches to ramp from idle")
@@ -131,12 +137,18 @@ def main():
               "share of the work; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    if args.config in ("3", "5"):
+        print(json.dumps(bench_chunks(args)), flush=True)
+        return
+
     import torch
 
     import paged_kv_attention_page_amd as wa
     import wa_workloads as W
 
     wl = W.WORKLOADS["wan_kp4"]
+    if args.config == "share":
+        wl = W.scaled(wl, name="wan_kp4_share3", n_heads=3)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     L = wa.layout(wa.WA_BF16, wl.n_heads, wl.head_dim, wl.page_tokens, wl.n_pages + 1)
@@ -298,19 +310,21 @@ def main():
     # shifted along the page-offset direction (a concentrated pooled map; the
     # plain queries give a near-uniform one), with per-head thresholds
     # 0.50, 0.54, ..., 0.94.
-    sparse = sparse_pass(wa, W, wl, L, up, k_ctx, v_ctx, k_own, v_own, out, stream, args.steps,
-                         avg["attention"], torch)
+    share = args.config == "share"
+    sparse = None if share else sparse_pass(wa, W, wl, L, up, k_ctx, v_ctx, k_own, v_own, out,
+                                            stream, args.steps, avg["attention"], torch)
 
     # host-tier pass (after the sparse pass; not part of the step figure): the
     # first selected page lives in pinned host memory and is copied into the
     # spare slot while the attention over the other selected pages runs
-    tier = tier_pass(wa, wl, L, k_pool, v_pool, q, k_own, v_own, idx, spare, stream,
-                     min(args.steps, 20), paged_attn_ms, torch)
+    tier = None if share else tier_pass(wa, wl, L, k_pool, v_pool, q, k_own, v_own, idx, spare,
+                                        stream, min(args.steps, 20), paged_attn_ms, torch)
 
     attn_tflops = flops / (avg["attention"] * 1e-3) / 1e12
     sg_gbps = (bytes_select + bytes_gather) / (avg["select_gather"] * 1e-3) / 1e9
     value = flops / (ms_per_step * 1e-3) / 1e12
-    traffic = load_traffic(args.traffic, wa.kernel_source("k_attn_bf16.hip"))
+    # the committed counter summary covers the 12-head launch only
+    traffic = None if share else load_traffic(args.traffic, wa.kernel_source("k_attn_bf16.hip"))
 
     result = {
         "metric": "block-attn TFLOP/s (MFMA %) + select/gather HBM GB/s at Kp=4, 49,920-tok KV",
@@ -326,12 +340,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "wan_kp4: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, "
-                        "16 resident pages, K_p=4, 4,680-query chunk, 49,920+4,680 keys, "
-                        "1 denoising step",
+            "workload": ("wan_kp4: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, "
+                         "16 resident pages, K_p=4, 4,680-query chunk, 49,920+4,680 keys, "
+                         "1 denoising step") if not share else
+                        ("wan_kp4_share3: one GPU's share of the Wan2.1-1.3B-shaped layer "
+                         "head-sharded over 4 GPUs: 3 heads x 128, 12,480-token pages, 16 "
+                         "resident pages, K_p=4, 4,680-query chunk, 49,920+4,680 keys, 1 "
+                         "denoising step (57 query-block x head items: the split launch)"),
             "n_heads": wl.n_heads, "head_dim": wl.head_dim, "page_tokens": wl.page_tokens,
             "pages": wl.n_pages, "k_p": wl.k_p, "n_q": wl.n_q, "n_ctx": wl.n_ctx,
-            "n_keys": n_k, "parallelism": "single GPU",
+            "n_keys": n_k,
+            "parallelism": "single GPU" if not share else "1 GPU's share of 4-way head sharding",
         },
         "roofline": {
             "bound": "mfma",
@@ -371,6 +390,8 @@ def main():
         "sparse": sparse,
         "tier": tier,
         "flops_per_step": flops,
+        "attention_split_launch": bool(wa.wa_attention_workspace_bytes(L, wl.n_q, wl.n_ctx,
+                                                                        wl.n_q) > 0),
         "cpu_baseline": None,
     }
 
@@ -378,6 +399,170 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means,
                                               args.cpu_seconds, torch)
     print(json.dumps(result), flush=True)
+
+
+def roofline_mfma(flops, ms, traffic=None):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": "k_attn_bf16", "achieved": round(tf, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic}
+
+
+def bench_chunks(args):
+    """Configs 3 and 5: whole chunks of the block-diffusion cadence (Inferix
+    summary, section 3.4, Steps 3 and 4): per chunk, select + gather once, then
+    T = 4 denoising steps of attention, each with fresh queries and own K/V
+    over the same gathered pages; config 5 then appends one new page (the
+    pool grows from 128 to 136 pages over 8 chunks).  One timed step = one
+    chunk; `value` = attention FLOPs of the chunk / chunk time."""
+    import torch
+
+    import paged_kv_attention_page_amd as wa
+    import wa_workloads as W
+
+    long_h = args.config == "5"
+    wl = W.WORKLOADS["long_horizon" if long_h else "full_history"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L = wa.layout(wa.WA_BF16, wl.n_heads, wl.head_dim, wl.page_tokens, wl.max_pages)
+    T = wl.steps
+    n_chunks = wl.chunks
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16).to(dev)
+
+    shape = (L.max_pages, wl.page_tokens, wl.n_heads, wl.head_dim)
+    k_pool = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    means = torch.zeros(L.max_pages, wl.n_heads, wl.head_dim, dtype=torch.float64, device=dev)
+    ws_append = torch.empty(wa.wa_append_workspace_bytes(L), dtype=torch.uint8, device=dev)
+    for j in range(wl.max_pages):
+        k, v = W.page_kv(wl, j)
+        k_pool[j].copy_(up(k))
+        v_pool[j].copy_(up(v))
+    for j in range(wl.n_pages):
+        wa.wa_append_page(L, k_pool[j], v_pool[j], k_pool, v_pool, j, means, workspace=ws_append)
+    # pages appended after chunk c (config 5): page n_pages + c, from a staging copy
+    new_pages = [(k_pool[wl.n_pages + c].clone(), v_pool[wl.n_pages + c].clone())
+                 for c in range(n_chunks * wl.appended_per_chunk)]
+    qkv = [[tuple(up(x) for x in W.chunk_qkv(wl, c, t)) for t in range(T)]
+           for c in range(n_chunks)]
+    idx = torch.empty(wl.k_p, dtype=torch.int32, device=dev)
+    max_cand = wl.n_pages + (n_chunks - 1) * wl.appended_per_chunk
+    ws_sel = torch.empty(wa.wa_select_workspace_bytes(L, wl.n_q, max_cand), dtype=torch.uint8,
+                         device=dev)
+    ws_attn = torch.empty(max(16, wa.wa_attention_workspace_bytes(L, wl.n_q, wl.n_ctx, wl.n_q)),
+                          dtype=torch.uint8, device=dev)
+    ctx_shape = (wl.n_ctx, wl.n_heads, wl.head_dim)
+    k_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
+    v_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
+    out = torch.empty((wl.n_q, wl.n_heads, wl.head_dim), dtype=torch.bfloat16, device=dev)
+    cands = [torch.arange(wl.n_pages + c * wl.appended_per_chunk, dtype=torch.int32, device=dev)
+             for c in range(n_chunks)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n_k = wl.n_ctx + wl.n_q
+    flops_step = attention_flops(wl.n_q, n_k, wl.head_dim, wl.n_heads)
+    page_bytes = wl.page_tokens * wl.n_heads * wl.head_dim * 2
+    row_means = wl.n_heads * wl.head_dim * 8
+
+    def chunk(c, ev=None):
+        """ev: T + 3 events (select+gather start, attention boundaries, append end)."""
+        cand = cands[c]
+        if ev is not None:
+            ev[0].record(stream)
+        wa.wa_select_pages(L, qkv[c][0][0], means, wl.k_p, cand=cand, out_idx=idx,
+                           workspace=ws_sel, stream=stream)
+        wa.wa_gather(L, k_pool, v_pool, idx, wl.k_p, k_ctx, v_ctx, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        for t in range(T):
+            q, ko, vo = qkv[c][t]
+            wa.wa_block_attention(L, q, k_ctx, v_ctx, ko, vo, wl.softmax_scale,
+                                  out_dtype=wa.WA_BF16, out=out, workspace=ws_attn, stream=stream)
+            if ev is not None:
+                ev[2 + t].record(stream)
+        for a in range(wl.appended_per_chunk):
+            slot = wl.n_pages + c * wl.appended_per_chunk + a
+            kn, vn = new_pages[c * wl.appended_per_chunk + a]
+            wa.wa_append_page(L, kn, vn, k_pool, v_pool, slot, means, workspace=ws_append,
+                              stream=stream)
+        if ev is not None:
+            ev[2 + T].record(stream)
+
+    for w in range(args.warmup):
+        chunk(w % n_chunks)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(T + 3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        chunk(k % n_chunks, evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_chunk = (t1 - t0) * 1e3 / args.steps
+    sg = [e[0].elapsed_time(e[1]) for e in evs]
+    att = [e[1 + t].elapsed_time(e[2 + t]) for e in evs for t in range(T)]
+    app = [e[1 + T].elapsed_time(e[2 + T]) for e in evs] if wl.appended_per_chunk else []
+    att_ms = float(np.mean(att))
+    sel_bytes = [wl.n_q * wl.n_heads * wl.head_dim * 2 + cands[k % n_chunks].numel() * row_means
+                 + 4 * wl.k_p for k in range(args.steps)]
+    sg_bytes = float(np.mean(sel_bytes)) + 2 * 2 * wl.k_p * page_bytes
+    sg_ms = float(np.mean(sg))
+    value = T * flops_step / (ms_chunk * 1e-3) / 1e12
+    name = "long_horizon" if long_h else "full_history"
+    desc = ("long_horizon: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, 128 "
+            "resident pages growing to 136 (one appended per chunk), K_p=4 selected over every "
+            "resident page, 4,680-query chunks, 49,920+4,680 keys, 8 chunks x 4 denoising steps"
+            if long_h else
+            "full_history: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, 6 "
+            "resident pages all attended (K_p=6), 4,680-query chunk, 74,880+4,680 keys, 4 "
+            "denoising steps with fresh queries and own K/V")
+    result = {
+        "metric": "block-attn TFLOP/s (MFMA %) + select/gather HBM GB/s, " + name,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_chunk, 4),
+        "step": "one chunk: select + gather, %d attention steps%s" % (
+            T, ", append of one page" if wl.appended_per_chunk else ""),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "n_heads": wl.n_heads, "head_dim": wl.head_dim,
+                   "page_tokens": wl.page_tokens, "pages": wl.n_pages,
+                   "pages_max": wl.max_pages, "k_p": wl.k_p, "n_q": wl.n_q, "n_ctx": wl.n_ctx,
+                   "n_keys": n_k, "steps_per_chunk": T, "chunks": n_chunks,
+                   "parallelism": "single GPU"},
+        "roofline": roofline_mfma(flops_step, att_ms),
+        "attention_ms_per_step": {"mean": round(att_ms, 4),
+                                  "median": round(float(np.median(att)), 4),
+                                  "min": round(float(np.min(att)), 4)},
+        "attention_target_ms": round(flops_step / (0.6 * PEAK_BF16_TFLOPS * 1e12) * 1e3, 4),
+        "select_gather": {"bytes": int(sg_bytes), "ms": round(sg_ms, 4),
+                          "GB/s": round(sg_bytes / (sg_ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(sg_bytes / (sg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "flops_per_attention_step": flops_step,
+        "cpu_baseline": None,
+    }
+    if app:
+        app_ms = float(np.mean(app))
+        app_bytes = 2 * 2 * page_bytes + row_means
+        result["append"] = {"bytes": app_bytes, "ms": round(app_ms, 4),
+                            "GB/s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1)}
+        result["pool_bytes"] = {"first_chunk": 2 * wl.n_pages * page_bytes,
+                                "after_last_chunk": 2 * wl.max_pages * page_bytes}
+    if not args.no_cpu_baseline:
+        c_last = (args.steps - 1) % n_chunks
+        q_h, ko_h, vo_h = W.chunk_qkv(wl, c_last, T - 1)
+        result["cpu_baseline"] = cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means,
+                                              args.cpu_seconds, torch,
+                                              n_resident=cands[c_last].numel())
+    return result
 
 
 def sparse_pass(wa, W, wl, L, up, k_ctx, v_ctx, k_own, v_own, out, stream, steps, dense_ms,
@@ -555,12 +740,13 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch):
+def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch,
+                 n_resident=None):
     """The fp64 oracle's attention on a bounded sample of query rows (all heads),
     on the host cores, in the metric's unit (TFLOP/s); the other stages of the
     step (one page mean, the selection, the gather) timed once each beside it."""
     import oracle
-    oracle.build(force=False)
+    oracle.use_native()          # gcc -O3 -march=native, built on this host
     sel = idx.cpu().numpy()
     k_ctx = np.ascontiguousarray(k_pool[torch.from_numpy(sel).long()].view(torch.uint16).cpu()
                                  .numpy().reshape(-1, wl.n_heads, wl.head_dim))
@@ -584,7 +770,8 @@ def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch
     t0 = time.perf_counter()
     oracle.page_mean(k_ctx[:wl.page_tokens])
     stages["append_page_mean"] = time.perf_counter() - t0
-    pm = np.ascontiguousarray(means[:wl.n_pages].cpu().numpy())
+    n_resident = wl.n_pages if n_resident is None else n_resident
+    pm = np.ascontiguousarray(means[:n_resident].cpu().numpy())
     t0 = time.perf_counter()
     oracle.select_pages(q_h, pm, wl.k_p)
     stages["select"] = time.perf_counter() - t0
@@ -600,13 +787,14 @@ def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
+        "build": "gcc -O3 -march=native -fopenmp (fp64, OpenMP over rows and heads)",
         "sample": "block attention of %d of %d query rows x %d heads over %d keys (fp64, "
                   "%.1f s)" % (len(rows), wl.n_q, wl.n_heads, n_k, dt),
         "stages_s": {k: round(v, 4) for k, v in stages.items()},
         "stages_note": "the oracle once each: the mean key of one page, the selection over "
                        "the %d resident pages (mean query, scores, top-%d), the gather of the "
                        "K and V of %d pages (single-threaded; attention uses the cores above)"
-                       % (wl.n_pages, wl.k_p, wl.k_p),
+                       % (n_resident, wl.k_p, wl.k_p),
         "nproc": os.cpu_count(),
         "cpu_model": cpu_model(),
     }

@@ -93,7 +93,7 @@ typedef int32_t wa_status;
 #define WA_HSA_OWN_BLOCK 64
 #define WA_HSA_Q_BLOCK 256
 #define WA_MAX_HSA_BLOCKS 2048   /* key blocks of one selection */
-#define WA_HSA_MAX_HEAD_DIM 256  /* head_dim of a selection */
+#define WA_HSA_MAX_HEAD_DIM 128  /* head_dim of a selection (64 and 128 tested, bf16 and fp32) */
 #define WA_MAX_SPARSE_TILES 4096 /* 64-key tiles of one sparse attention */
 
 typedef struct wa_layout {
@@ -237,8 +237,14 @@ wa_status wa_gather(const wa_layout *layout, const void *k_pool, const void *v_p
  * One softmax over both segments, no mask of any kind.
  *
  * q, out: [n_q][H][d]; k_ctx, v_ctx: [n_ctx][H][d]; k_own, v_own: [n_own][H][d].
- * WA_BF16 inputs are multiplied on the matrix cores with fp32 accumulation;
- * the probabilities are rounded to bf16 before the value product.
+ * Precision (WA_BF16): the queries and keys enter the matrix-core products
+ * exactly as given (bf16 x bf16 products, fp32 accumulation); the softmax
+ * scale is applied to each fp32 score by one fused multiply-add (together
+ * with log2(e) and the running maximum) before the exponential, so a score
+ * carries only fp32 rounding.  The probabilities are rounded to bf16 before
+ * the value product (fp32 accumulation), and the row sum is taken from the
+ * same rounded probabilities.  WA_F32 inputs are computed in fp32
+ * throughout.
  * out_dtype: WA_F32, or WA_BF16 when layout.dtype is WA_BF16.
  * lse: device [H][n_q] float, or NULL.  n_ctx or n_own may be 0 (the
  * matching pointers may then be NULL).  out must not overlap any input.

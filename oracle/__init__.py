@@ -24,7 +24,7 @@ the order the pages give them:
   cumulative-mass block selection, attention over the selected blocks) --
   WorldAttention review, "HSA: Dual Branches of Linear + Sparse"; these
   compose the C attention with numpy, and their pins are planted with
-  mistakes in ``tests/test_oracle_mutations_hsa.py``.
+  mistakes in ``tests/test_oracle_mutations_py.py``.
 
 Parity status of each function: pinned by ``tests/test_oracle_pins.py``
 (closed forms, invariants, brute force, and a textbook library routine).
@@ -41,20 +41,33 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wa_oracle.c")
 _LIB = os.path.join(_HERE, "libwa_oracle.so")
+_LIB_NATIVE = os.path.join(_HERE, "libwa_oracle_native.so")
 
 F32, BF16 = 0, 1
 
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (fp64, OpenMP over rows and heads)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+def build(force: bool = True, native: bool = False) -> str:
+    """Compile the oracle with gcc -O3 (fp64, OpenMP over rows and heads).
+
+    native=True builds a copy tuned for the host it runs on (-march=native,
+    for the CPU-baseline timing; built where it runs, never shipped between
+    machines); the tests use the portable build."""
+    lib = _LIB_NATIVE if native else _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
+        arch = ["-march=native"] if native else []
+        subprocess.check_call(["gcc", "-O3"] + arch + ["-fopenmp", "-fPIC", "-shared", "-std=c11",
                                "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
+
+
+def use_native() -> None:
+    """Build the host-tuned copy here and make every later call use it."""
+    global _lib
+    _lib = configure(ctypes.CDLL(build(force=True, native=True)))
 
 
 def configure(lib):
@@ -97,8 +110,13 @@ def _dtype_code(x: np.ndarray) -> int:
 
 
 def n_threads() -> int:
-    """Threads for the attention loop: the host's cores, at most 16."""
-    return max(1, min(16, os.cpu_count() or 1))
+    """Threads for the attention loop: every core this process may run on,
+    at most 16 (the CPU share of one GPU on the measurement boxes)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 # ----------------------------------------------------------------------------

@@ -131,7 +131,9 @@ void wao_prompt_cosine(const float *chunk_prompts, const float *cur, int n_chunk
             dot += (double)cur[e] * (double)pm[e];
             nn += (double)pm[e] * (double)pm[e];
         }
-        cos_out[m] = dot / (sqrt(pp) * sqrt(nn));
+        /* Reading: an embedding of zero norm has no direction, so its cosine
+         * is -inf (that chunk ranks last; ties go to the lower chunk id). */
+        cos_out[m] = (pp > 0.0 && nn > 0.0) ? dot / (sqrt(pp) * sqrt(nn)) : -INFINITY;
     }
 }
 

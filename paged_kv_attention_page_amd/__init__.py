@@ -26,7 +26,8 @@ __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "W
            "wa_select_pages", "wa_select_window", "wa_gather", "wa_attention_workspace_bytes",
            "wa_block_attention", "wa_paged_attention", "hsa_shape", "wa_hsa_workspace_bytes",
            "wa_hsa_select", "wa_sparse_workspace_bytes", "wa_sparse_attention",
-           "wa_page_in", "wa_page_out", "wa_merge_attention", "wa_status_string"]
+           "wa_page_in", "wa_page_out", "wa_merge_attention", "wa_status_string",
+           "use_library"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -68,6 +69,16 @@ class WaError(RuntimeError):
 
 def library_path() -> str:
     return _LIB_PATH
+
+
+def use_library(path: str | None = None) -> str:
+    """Point the binding at another build of the library (e.g. the debug copy
+    libwa_poison.so); None goes back to libwa.so.  Returns the previous path."""
+    global _LIB_PATH, _lib
+    prev = _LIB_PATH
+    _LIB_PATH = path if path is not None else os.path.join(_HERE, "libwa.so")
+    _lib = None
+    return prev
 
 
 def kernel_source(name: str) -> bytes:

@@ -12,6 +12,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libwa.so")
+# Debug copy of the library whose attention kernel fills its LDS stages with
+# NaN before every refill (WA_DEBUG_POISON); only a GPU test loads it.
+LIB_POISON = os.path.join(PKG, "libwa_poison.so")
+POISON_SRC = "k_attn_bf16.hip"
 
 ARCH = "gfx950"
 # Packed fp32 instructions stay off: plain fp32 arithmetic only.
@@ -41,31 +45,39 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+def _compile(src: str, poison: bool = False) -> str:
+    obj = os.path.join(OBJ, os.path.basename(src) + (".poison.o" if poison else ".o"))
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + HIP_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + lang + \
-        ["-c", src, "-o", obj]
+    cmd = [hipcc()] + HIP_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + \
+        (["-DWA_DEBUG_POISON"] if poison else []) + lang + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libwa.so; always rebuilds."""
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libwa.so and its poison-checking debug
+    copy libwa_poison.so; always rebuilds."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    poison_src = os.path.join(CSRC, POISON_SRC)
+    with ThreadPoolExecutor(min(8, len(srcs) + 1)) as ex:
+        objs = list(ex.map(_compile, srcs))
+        poison_obj = ex.submit(_compile, poison_src, True).result()
+    _link(objs, LIB)
+    _link([poison_obj if o.endswith(POISON_SRC + ".o") else o for o in objs], LIB_POISON)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", LIB_POISON)
     return LIB
 
 

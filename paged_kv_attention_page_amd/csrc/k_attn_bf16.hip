@@ -22,8 +22,9 @@
 //    max / sum live in one lane pair (one permlane32 swap) and rescaling the
 //    output is a per-lane multiply.
 //  * O^T += V^T P^T: P comes straight from the S^T accumulator layout
-//    (exp2 of S - m, rounded to bf16, with S in base-2 units because the
-//    Q fragments carry scale*log2(e)); V^T operands are read
+//    (p = exp2(S * c - m) with c = scale * log2(e), one fused multiply-add
+//    per score on the exact bf16 products, rounded to bf16); V^T operands
+//    are read
 //    with ds_read_b64_tr_b16, whose 16-lane 4x16 -> 16x4 transpose turns the
 //    row-major V tile into the key-contiguous operand, in the key order that
 //    matches P.
@@ -59,33 +60,60 @@ static constexpr int kStages = 4;         // LDS ring depth (tiles)
 static constexpr int kTileElems = kBN * kD;
 static constexpr int kRowsPerWave = kBN / kWaves;   // tile rows each wavefront copies
 static constexpr int kCopies = kRowsPerWave / 4;    // 1 KB copies per tensor per wavefront
-// Scores are kept in base-2 units: the Q fragments carry the factor
-// c = softmax_scale * log2(e) (one bf16 rounding of q * c), so p = 2^(s - m).
-// The probabilities of a sub-tile are taken against a reference max m (the
-// row max of the segment's first sub-tile) that only moves when a row's new
-// probabilities sum past 2^8 (some score more than 8 above m, or an
-// overflow): O and l are then rescaled and the sub-tile's probabilities
-// recomputed.  The result is exact either way, since O and l always share the
-// reference max, and no per-sub-tile maximum is needed.  Every chain of score
-// products starts from the accumulator value -m, so the scores arrive already
-// shifted and the exponentials take them as they are (no vector operation
-// per score before the exponential).
+// The matrix cores multiply the exact bf16 queries and keys (fp32
+// accumulation, each chain of score products starts from zero), and the
+// softmax runs in base-2 units: p = 2^(s c - m) with c = softmax_scale *
+// log2(e), the scaling fused into one multiply-add per score before the
+// exponential, so the only roundings of a score are those of the fp32
+// accumulation and of that multiply-add.  (Scaling the queries by c in bf16
+// before the products saves the multiply-add but rounds every q * c to 8
+// bits, which moves the log-sum-exp by up to 2^-8 scale sum_d |q_d k_d|.)
+// The probabilities of a sub-tile are taken against a reference max m (base-2
+// units: c times the row max of the segment's first sub-tile) that only moves
+// when a row's new probabilities sum past 2^8 (some score more than 8 above
+// m, or an overflow): O and l are then rescaled and the sub-tile's
+// probabilities recomputed.  The result is exact either way, since O and l
+// always share the reference max, and no per-sub-tile maximum is needed.
 static constexpr float kSumLimit = 256.f;
 // LDS operands are read this many matrix products ahead of their use (of the
-// 8 per region).  With the -m start vector (16 registers) live, 3 is the
-// deepest that fits 256 registers without spills in every mode: on the
-// Wan-shaped launch 3 measured 1.311 ms and 5 (with spills) 1.306 ms; before
-// the start vector, 2 and 6 measured 1.420 and 1.367 ms.
-static constexpr int kPrefetch = 3;
+// 8 per region); 6 fits 256 registers without spills in every mode.
+static constexpr int kPrefetch = 6;
+// Debug build (WA_DEBUG_POISON): the whole K/V ring is filled with NaN when
+// a block starts, and every stage is filled with NaN again by the
+// wavefronts that refill it, after the barrier that ends its last reads and
+// before its copies are issued.  A read of a stage whose tile has not landed
+// (a missing wait), of a stage nothing was copied into, or of a stage's
+// previous tile then carries NaN into the products; results that stay finite
+// and equal to the regular build's show that no such value reaches an output.
+#ifdef WA_DEBUG_POISON
+static constexpr bool kPoison = true;
+#else
+static constexpr bool kPoison = false;
+#endif
 static constexpr int kMaxSplitBlocks = 256;  // blocks of a split launch (partial slots)
 static constexpr int kMinSplitTiles = 16;    // fewest tiles per block worth a split
 static constexpr int kMaxBlocksPerItem = 32; // split blocks per (query block, head) item
 static constexpr int kMaxSlots = 64;         // pieces of one item a split may leave
 
+// Workgroups are dispatched to the 8 XCDs round robin (block b on XCD b % 8),
+// so XCD x runs n / 8 blocks, one more when x < n % 8.  Logical block
+// numbers are handed out in contiguous ranges per XCD, the XCDs taken in an
+// order that alternates those with one block more and those without: with
+// 228 items of 19 query blocks per head, every second range boundary then
+// falls on a head boundary, and only 4 of the 12 heads have their K/V read
+// through two L2s (7 with the XCDs in plain order).
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
     const int q = n >> 3, r = n & 7;
     const int x = bid & 7, i = bid >> 3;
-    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+    const int m = r < 8 - r ? r : 8 - r;
+    int start = 0;
+    for (int k = 0; k < 8; ++k) {
+        const int xk = k < 2 * m ? ((k & 1) ? r + (k >> 1) : (k >> 1))
+                                 : (r > 8 - r ? k - m : r + k - m);
+        if (xk == x) break;
+        start += q + (xk < r ? 1 : 0);
+    }
+    return start + i;
 }
 
 struct AttnArgs {
@@ -257,6 +285,11 @@ void k_attn_bf16(AttnArgs a) {
     // consecutive logical blocks run on one XCD (one L2): with the split, they
     // take consecutive runs of the same head's work
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    if constexpr (kPoison) {
+        // the whole ring holds NaN before anything is copied into it
+        for (int i = tid; i < 2 * kStages * kTileElems; i += kThreads) lds_ring[i] = 0x7fc0;
+        __syncthreads();
+    }
     const int64_t hd = (int64_t)a.n_heads * kD;
     const int n_keys = a.n_ctx + a.n_own;
     const int n_tiles = a.n_tiles;
@@ -380,6 +413,19 @@ void k_attn_bf16(AttnArgs a) {
         constexpr unsigned S = decltype(stage_tag)::value;
         const int t = MODE == 3 ? sp_tile(pos) : pos;
         constexpr unsigned OK = S * kTileBytes, OV = (kStages + S) * kTileBytes;
+        if constexpr (kPoison) {
+            // NaN over this wavefront's 8 rows (2 KB) of the K and V stage,
+            // written and waited for before the copies that refill them
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+            WA_LDS char *kr = (WA_LDS char *)(uintptr_t)(ld_base + OK) + 32 * lane;
+            WA_LDS char *vr = (WA_LDS char *)(uintptr_t)(ld_base + OV) + 32 * lane;
+            *(WA_LDS u32x4 *)kr = nan4;
+            *(WA_LDS u32x4 *)(kr + 16) = nan4;
+            *(WA_LDS u32x4 *)vr = nan4;
+            *(WA_LDS u32x4 *)(vr + 16) = nan4;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
         constexpr unsigned ROWS4 = 4 * kD * 2;    // four tile rows
         const int key0 = t * kBN;
         if (t != t_mid && t < t_full && (MODE != 2 || t >= t_ctx)) {
@@ -421,20 +467,16 @@ void k_attn_bf16(AttnArgs a) {
         dma16<OV + ROWS4>(vr[1], ld_base);
     };
 
-    // ---- this wavefront's 32 queries as B operands, in base-2 score units:
-    // qf[st] = bf16(c * Q[q0+lr][16st+8hb ..+7])
+    // ---- this wavefront's 32 queries as B operands, as given:
+    // qf[st] = Q[q0+lr][16st+8hb ..+7]
     bf16x8 qf[8];
     {
         const int row = q0 + lr;
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            if (row < a.n_q) {
-                const bf16x8 raw = *(const bf16x8 *)(a.q + (int64_t)row * hd + h * kD + 16 * st + 8 * hb);
-                bf16x8 scaled;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) scaled[e] = (__bf16)((float)raw[e] * c);
-                qf[st] = scaled;
-            } else
+            if (row < a.n_q)
+                qf[st] = *(const bf16x8 *)(a.q + (int64_t)row * hd + h * kD + 16 * st + 8 * hb);
+            else
                 qf[st] = (bf16x8)(__bf16)0.f;
         }
     }
@@ -445,7 +487,7 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
     float m = 0.f, l = 0.f;   // reference max (base-2 units), row sum
-    f32x16 cinit;             // -m in every element: start of each score chain
+    const f32x16 zero16 = {};  // start of each score chain (an inline constant)
 
     // ---- keys past the end (last tile only) get score -inf.  Their rows were
     // loaded as copies of the last key, so maxima taken before masking are
@@ -460,7 +502,7 @@ void k_attn_bf16(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
             if (8 * (i >> 2) + (i & 3) >= lim) s[i] = -INFINITY;
     };
-    // ---- region QK+SOFTMAX: sn = K Q^T - m of the sub-tile at koff (8 MFMAs)
+    // ---- region QK+SOFTMAX: sn = K Q^T of the sub-tile at koff (8 MFMAs)
     // interleaved with the exponentials of sc (2 elements per MFMA), P packed to
     // bf16 for the P V products, l accumulated from the bf16 values; then the
     // lazy-rescale test (see kSumLimit).  Operands are read kPf products
@@ -473,9 +515,9 @@ void k_attn_bf16(AttnArgs a) {
         const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? cinit : sn, 0, 0, 0);
-            const float p0 = __builtin_amdgcn_exp2f(sc[2 * st]);
-            const float p1 = __builtin_amdgcn_exp2f(sc[2 * st + 1]);
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero16 : sn, 0, 0, 0);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * st], c, -m));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * st + 1], c, -m));
             const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
             pb[st >> 2][2 * (st & 3)] = pr[0];
             pb[st >> 2][2 * (st & 3) + 1] = pr[1];
@@ -490,9 +532,9 @@ void k_attn_bf16(AttnArgs a) {
             float x = fmaxf(sc[0], sc[1]);
 #pragma unroll
             for (int i = 1; i < 8; ++i) x = fmaxf(x, fmaxf(sc[2 * i], sc[2 * i + 1]));
-            // the new reference max is m + dm; sn, already started from -m,
-            // is moved to it as well
-            const float dm = fmaxf(xhalf_max(x), 0.f);
+            // the new reference max is m + dm (x: the sub-tile's row max, in
+            // natural units)
+            const float dm = fmaxf(xhalf_max(x) * c - m, 0.f);
             const float corr = __builtin_amdgcn_exp2f(-dm);
             l *= corr;
 #pragma unroll
@@ -500,16 +542,11 @@ void k_attn_bf16(AttnArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[b][i] *= corr;
             m += dm;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                cinit[i] = -m;
-                sn[i] -= dm;
-            }
             lsub = 0.f;
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
-                const float p0 = __builtin_amdgcn_exp2f(sc[2 * st] - dm);
-                const float p1 = __builtin_amdgcn_exp2f(sc[2 * st + 1] - dm);
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * st], c, -m));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * st + 1], c, -m));
                 const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
                 pb[st >> 2][2 * (st & 3)] = pr[0];
                 pb[st >> 2][2 * (st & 3) + 1] = pr[1];
@@ -567,17 +604,13 @@ void k_attn_bf16(AttnArgs a) {
         for (int st = 0; st < 8; ++st)
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[st], qf[st], st == 0 ? zero : sa, 0, 0, 0);
         if (t_begin == mask_tile) mask_tail(sa, mask_key0);
-        // its row max is the first reference max (a masked sub-tile still
-        // holds at least one real key: the last tile's first key)
+        // its row max (times c) is the first reference max (a masked
+        // sub-tile still holds at least one real key: the last tile's first
+        // key)
         float x = fmaxf(sa[0], sa[1]);
 #pragma unroll
         for (int i = 1; i < 8; ++i) x = fmaxf(x, fmaxf(sa[2 * i], sa[2 * i + 1]));
-        m = xhalf_max(x);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sa[i] -= m;
-            cinit[i] = -m;
-        }
+        m = xhalf_max(x) * c;
 #pragma unroll
         for (int st = 0; st < kPf; ++st) ak[st] = read_k(kSubBytes, st);
     }

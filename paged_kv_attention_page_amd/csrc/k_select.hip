@@ -130,7 +130,10 @@ __global__ __launch_bounds__(256) void k_select_stage1(
         pp += a * a;
     }
     block_sum3(dot, nn, pp, lds);
-    if (threadIdx.x == 0) cosine[m] = dot / (sqrt(pp) * sqrt(nn));
+    // a prompt of zero norm has no direction: its cosine is -inf, so that
+    // chunk ranks after every other (ties to the lower chunk id), and a zero
+    // current prompt leaves the chunks in id order
+    if (threadIdx.x == 0) cosine[m] = (pp > 0.0 && nn > 0.0) ? dot / (sqrt(pp) * sqrt(nn)) : -INFINITY;
 }
 
 // Rank the chunks by (cosine desc, id asc) and write the first n_keep chunk

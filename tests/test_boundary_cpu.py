@@ -314,7 +314,8 @@ def test_hsa_workspace_size(lib):
     assert lib.wa_hsa_workspace_bytes(L(), 0, 64, 64) == 0
     assert lib.wa_hsa_workspace_bytes(L(), 64, 0, 0) == 0
     assert lib.wa_hsa_workspace_bytes(L(), 64, 128 * 2048, 64) == 0     # 2,049 key blocks
-    assert lib.wa_hsa_workspace_bytes(L(H=2, d=512), 64, 64, 64) == 0   # head_dim > 256
+    assert lib.wa_hsa_workspace_bytes(L(H=2, d=512), 64, 64, 64) == 0   # head_dim > 128
+    assert lib.wa_hsa_workspace_bytes(L(H=2, d=256), 64, 64, 64) == 0   # head_dim > 128
     assert lib.wa_hsa_workspace_bytes(None, 64, 64, 64) == 0
 
 
@@ -348,7 +349,8 @@ def test_hsa_select_rejects(lib):
     assert _hsel(lib, count=ctypes.c_void_p(0x10002)) == E
     assert _hsel(lib, ws_bytes=1024) == E                    # workspace too small
     assert _hsel(lib, n_ctx=100) == U                        # context not whole tiles
-    assert _hsel(lib, lay=L(H=2, d=512)) == U                # head_dim > 256
+    assert _hsel(lib, lay=L(H=2, d=512)) == U                # head_dim > 128
+    assert _hsel(lib, lay=L(H=2, d=256)) == U                # head_dim > 128
     assert _hsel(lib, n_ctx=128 * 2048, n_own=64) == U       # 2,049 key blocks
     assert _hsel(lib, lay=L(dtype=7)) == U
 

@@ -133,7 +133,10 @@ def test_small_bf16_pipeline():
 
 def test_wan_kp4_full_size_sampled_rows():
     """Wan2.1-1.3B-shaped layer: 12 heads, 12,480-token pages, 16 pages, K_p 4,
-    4,680 queries, 49,920 + 4,680 keys; attention checked on sampled rows."""
+    4,680 queries, 49,920 + 4,680 keys, in the launch configuration the bench
+    times.  Attention (fp32 and bf16 outputs, lse) checked on every row of one
+    whole 256-query block and of the ragged last block (72 rows), for every
+    head, plus 40 rows spread over the rest."""
     wl = W.WORKLOADS["wan_kp4"]
     run = PoolRun(wl)
     for j in range(wl.n_pages):
@@ -142,7 +145,10 @@ def test_wan_kp4_full_size_sampled_rows():
     q, ko, vo = W.chunk_qkv(wl, 0, 0)
     idx, _ = check_select(run, q, to_device(q), wl.k_p)
     k_ctx, v_ctx, hk, hv = check_gather(run, idx, wl.k_p)
-    rows = rows_sample(wl.n_q, 40)
+    block = np.arange(9 * 256, 10 * 256, dtype=np.int64)           # a whole interior block
+    tail = np.arange((wl.n_q // 256) * 256, wl.n_q, dtype=np.int64)  # the ragged last block
+    assert tail.size == 72
+    rows = np.unique(np.concatenate([rows_sample(wl.n_q, 40), block, tail]))
     check_attention(wl, q, hk, hv, ko, vo, k_ctx, v_ctx, rows=rows)
 
 
@@ -194,7 +200,7 @@ def test_full_history_steps():
     for step in range(wl.steps):
         q, ko, vo = W.chunk_qkv(wl, 0, step)
         got = check_attention(wl, q, hk, hv, ko, vo, k_ctx, v_ctx, rows=rows,
-                              out_dtypes=[wa.WA_F32])
+                              out_dtypes=[wa.WA_BF16, wa.WA_F32])
         if step == 0:
             hist, _ = oracle.attention(q, hist_k, hist_v, ko, vo, wl.softmax_scale, rows=rows)
             assert np.abs(hist - got).max() < 1e-12
@@ -242,12 +248,18 @@ def test_long_horizon_chunks():
         assert to_bits(v_ctx).tobytes() == hv.tobytes()
         for step in range(wl.steps):
             q, ko, vo = W.chunk_qkv(wl, c, step)
-            say("long horizon chunk", c, "step", step, "attention")
-            out = wa.wa_block_attention(run.L, to_device(q), k_ctx, v_ctx, to_device(ko),
-                                        to_device(vo), wl.softmax_scale, out_dtype=wa.WA_BF16)
-            ref_out, _ = oracle.attention(q, hk, hv, ko, vo, wl.softmax_scale, rows=rows)
-            err = np.abs(to_f64(out)[rows] - ref_out).max()
-            assert err <= tol, "chunk %d step %d: attention max |err| %g" % (c, step, err)
+            ref_out, ref_lse = oracle.attention(q, hk, hv, ko, vo, wl.softmax_scale, rows=rows)
+            # bf16 outputs every step, fp32 outputs and lse on the chunk's first step
+            for odt in ([wa.WA_BF16, wa.WA_F32] if step == 0 else [wa.WA_BF16]):
+                say("long horizon chunk", c, "step", step, "attention, out dtype", odt)
+                lse = torch.empty(wl.n_heads, wl.n_q, dtype=torch.float32, device="cuda")
+                out = wa.wa_block_attention(run.L, to_device(q), k_ctx, v_ctx, to_device(ko),
+                                            to_device(vo), wl.softmax_scale, out_dtype=odt,
+                                            lse=lse)
+                err = np.abs(to_f64(out)[rows] - ref_out).max()
+                assert err <= tol, "chunk %d step %d: attention max |err| %g" % (c, step, err)
+                lerr = np.abs(lse.cpu().double().numpy()[:, rows] - ref_lse).max()
+                assert lerr <= tol, "chunk %d step %d: lse max |err| %g" % (c, step, lerr)
         del k_ctx, v_ctx, hk, hv
         append(wl.n_pages + c)
     got_means = run.means.cpu().numpy()
@@ -295,4 +307,5 @@ def test_prompt_page_full_size():
     assert to_bits(k_ctx).tobytes() == hk.tobytes()
     assert to_bits(v_ctx).tobytes() == hv.tobytes()
     rows = rows_sample(wl.n_q, 8)
-    check_attention(wl, q, hk, hv, ko, vo, k_ctx, v_ctx, rows=rows, out_dtypes=[wa.WA_BF16])
+    check_attention(wl, q, hk, hv, ko, vo, k_ctx, v_ctx, rows=rows,
+                    out_dtypes=[wa.WA_BF16, wa.WA_F32])

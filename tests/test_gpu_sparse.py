@@ -113,6 +113,18 @@ def test_selection_matches_the_oracle():
         _check_selection(L, wl, q, kc, ko, tau, wl.softmax_scale)
 
 
+@pytest.mark.parametrize("dtype,head_dim", [(W.F32, 64), (W.F32, 128), (W.BF16, 64)],
+                         ids=["f32_d64", "f32_d128", "bf16_d64"])
+def test_selection_other_layouts(dtype, head_dim):
+    """The selection over fp32 inputs and head_dim 64 (the attention over the
+    lists is bf16 at head_dim 128 only; the selection takes any layout up to
+    head_dim 128)."""
+    wl = W.scaled(SMALL, name="hsa_%s_d%d" % (dtype, head_dim), dtype=dtype, head_dim=head_dim)
+    L = wa_layout(wl)
+    q, kc, _, ko, _ = _inputs(wl, [5, 0, 3, 7, 2], 576, 560, gain=8.0)
+    _check_selection(L, wl, q, kc, ko, [0.5, 0.8, 0.95], wl.softmax_scale)
+
+
 def test_selection_one_segment_only():
     """Context only (n_own = 0) and own keys only (n_ctx = 0)."""
     wl = SMALL

@@ -185,3 +185,84 @@ def test_tiered_step_full_size():
     v_ctx = np.concatenate([run.host_v[p] for p in idx])
     ref, _ = oracle.attention(q, k_ctx, v_ctx, ko, vo, wl.softmax_scale, rows=rows)
     assert np.abs(to_f64(out)[rows] - ref).max() <= attention_tolerance(wl)
+
+
+def test_tiered_step_on_growing_scores():
+    """The tiered step on scores far from unit variance: keys climb along one
+    direction that every query shares, so the scores rise to about 16 over the
+    768 context keys.  The merge weights each part by exp(lse_part - lse), so
+    this holds the parts' log-sum-exps, through the merged output and lse, to
+    the same bar as the outputs (one softmax over all the selected pages,
+    Inferix summary, section 3.4, Step 3; partial results accumulated as in
+    its "Ring Attention" paragraph)."""
+    wl = W.scaled(SMALL, name="tier_growing")     # 8 slots of 128 tokens; 6 hold data
+    L = wa.layout(wa.WA_BF16, wl.n_heads, wl.head_dim, wl.page_tokens, wl.max_pages)
+    P_t, n_own, n_q = wl.page_tokens, 90, 70
+    rng = np.random.default_rng([wl.wid, 31])
+    u = np.ones(wl.head_dim, np.float32) / np.sqrt(wl.head_dim)
+
+    def rows(n, ramp):
+        x = 0.25 * rng.standard_normal((n, wl.n_heads, wl.head_dim), dtype=np.float32)
+        if ramp is not None:
+            x += (ramp[:, None, None] * u[None, None, :]).astype(np.float32)
+        return W.encode(wl, x)
+
+    n_sel = 6
+    n_ctx = n_sel * P_t
+    ramp = 0.06 * np.arange(n_ctx + n_own, dtype=np.float32)
+    q = rows(n_q, np.full(n_q, 4.0, np.float32))
+    kc, ko = rows(n_ctx, ramp[:n_ctx]), rows(n_own, ramp[n_ctx:])
+    vc, vo = rows(n_ctx, None), rows(n_own, None)
+    shape = (wl.max_pages, P_t, wl.n_heads, wl.head_dim)
+    k_pool = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.zeros_like(k_pool)
+    for j in range(n_sel):
+        k_pool[j].copy_(to_device(kc[j * P_t:(j + 1) * P_t]))
+        v_pool[j].copy_(to_device(vc[j * P_t:(j + 1) * P_t]))
+    # selected pages in a non-temporal order; pages 5 and 1 live in host memory
+    idx = [3, 5, 0, 1, 4, 2]
+    on_host = {5: 0, 1: 1}
+    hk, hv = _host_pool(wl, 2)
+    for p, h in on_host.items():
+        wa.wa_page_out(L, k_pool, v_pool, p, hk, hv, h)
+    torch.cuda.synchronize()
+    for p in on_host:
+        k_pool[p].zero_()
+        v_pool[p].zero_()
+    spare = [6, 7]
+    resident = [p for p in idx if p not in on_host]
+    missing = [p for p in idx if p in on_host]
+    copy = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    copy.wait_stream(main)
+    with torch.cuda.stream(copy):
+        for p, s in zip(missing, spare):
+            wa.wa_page_in(L, hk, hv, on_host[p], k_pool, v_pool, s, stream=copy)
+    done = torch.cuda.Event()
+    done.record(copy)
+    qd, kod, vod = to_device(q), to_device(ko), to_device(vo)
+    lse_a = torch.empty(wl.n_heads, n_q, dtype=torch.float32, device="cuda")
+    lse_b = torch.empty_like(lse_a)
+    say("tiered step on growing scores: resident", resident, "copied in", missing)
+    out_a = wa.wa_paged_attention(L, qd, k_pool, v_pool,
+                                  torch.tensor(resident, dtype=torch.int32, device="cuda"),
+                                  len(resident), kod, vod, wl.softmax_scale, out_dtype=wa.WA_F32,
+                                  lse=lse_a)
+    main.wait_event(done)
+    out_b = wa.wa_paged_attention(L, qd, k_pool, v_pool,
+                                  torch.tensor(spare, dtype=torch.int32, device="cuda"),
+                                  len(spare), None, None, wl.softmax_scale, out_dtype=wa.WA_F32,
+                                  lse=lse_b)
+    lse = torch.empty_like(lse_a)
+    out = wa.wa_merge_attention(L, out_a, lse_a, out_b, lse_b, wa.WA_F32, lse=lse)
+    out16 = wa.wa_merge_attention(L, out_a, lse_a, out_b, lse_b, wa.WA_BF16)
+    torch.cuda.synchronize()
+    order = [p for p in idx]                       # keys in the order attended: any order
+    k_sel = np.concatenate([kc[p * P_t:(p + 1) * P_t] for p in order])
+    v_sel = np.concatenate([vc[p * P_t:(p + 1) * P_t] for p in order])
+    ref, ref_lse = oracle.attention(q, k_sel, v_sel, ko, vo, wl.softmax_scale)
+    assert ref_lse.max() > 14.0, "scores should climb far beyond unit variance"
+    tol = attention_tolerance(wl)
+    assert np.abs(to_f64(out) - ref).max() <= tol
+    assert np.abs(to_f64(out16) - ref).max() <= tol
+    assert np.abs(lse.cpu().double().numpy() - ref_lse).max() <= tol

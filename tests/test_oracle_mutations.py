@@ -27,8 +27,8 @@ MUTATIONS = {
                                       "s += qbar[col] * kbar[hd - 1 - col];"),
     "top-k keeps the lowest score": ("return sa > sb ||", "return sa < sb ||"),
     "top-k tie goes to the higher id": ("(sa == sb && ia < ib)", "(sa == sb && ia > ib)"),
-    "cosine forgets a square root": ("cos_out[m] = dot / (sqrt(pp) * sqrt(nn));",
-                                     "cos_out[m] = dot / (sqrt(pp) * nn);"),
+    "cosine forgets a square root": ("dot / (sqrt(pp) * sqrt(nn)) : -INFINITY;",
+                                     "dot / (sqrt(pp) * nn) : -INFINITY;"),
     "candidates take pages of the rank, not the chunk":
         ("chunk_pages[(int64_t)chunks_out[r] * pages_per_chunk + p];",
          "chunk_pages[(int64_t)r * pages_per_chunk + p];"),

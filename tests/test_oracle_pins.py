@@ -206,6 +206,26 @@ def test_cosine_closed_forms(oracle_lib):
     assert oracle_lib.prompt_cosine(np.stack([e1]), e0)[0] == 0.0
 
 
+def test_zero_norm_prompt_ranks_last(oracle_lib):
+    """Reading: a prompt embedding of zero norm has no direction, so its
+    cosine is -inf.  A zero chunk prompt ranks after every other chunk (two
+    such chunks in id order); a zero current prompt leaves every chunk at -inf,
+    so the kept chunks are the lowest ids."""
+    a, b, c = f32(32), f32(32), f32(32)
+    z = np.zeros(32, np.float32)
+    cp = np.stack([z, a, z, b, c])
+    cos = oracle_lib.prompt_cosine(cp, a)
+    assert np.isneginf(cos[0]) and np.isneginf(cos[2]) and np.isfinite(cos[[1, 3, 4]]).all()
+    pages = np.arange(10, dtype=np.int32).reshape(5, 2)
+    chunks, cand = oracle_lib.prompt_candidates(cos, pages, 5)
+    assert chunks.tolist()[:3] == sorted([1, 3, 4], key=lambda m: (-cos[m], m))
+    assert chunks.tolist()[3:] == [0, 2]
+    assert cand.tolist() == [p for m in chunks for p in (2 * m, 2 * m + 1)]
+    cos0 = oracle_lib.prompt_cosine(cp, z)
+    assert np.isneginf(cos0).all()
+    assert oracle_lib.prompt_candidates(cos0, pages, 3)[0].tolist() == [0, 1, 2]
+
+
 def test_prompt_stage_recalls_the_matching_chunk(oracle_lib):
     """A current prompt equal to past chunk m0's prompt ranks m0 first."""
     wl = W.scaled(W.WORKLOADS["prompt_page"], emb_dim=256)
