@@ -185,6 +185,25 @@ wa_status wa_select_pages(const wa_layout *layout, const void *q, int32_t n_q,
                           void *stream);
 
 /*
+ * wa_select_pages without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The selection's workspace is a fixed
+ * array inside the library's device image, one per GPU the library runs on,
+ * held until the process ends; the call allocates nothing (its first call on
+ * a device looks the array's address up).  Same arguments, results and
+ * errors as wa_select_pages, plus: a selection whose workspace
+ * (wa_select_workspace_bytes) exceeds WA_SELECT_NOALLOC_MAX_WORKSPACE ->
+ * WA_ERR_UNSUPPORTED.  All calls on one GPU share the array, so calls that
+ * overlap on one GPU (concurrent streams, threads) race; calls ordered on
+ * one stream do not.
+ */
+#define WA_SELECT_NOALLOC_MAX_WORKSPACE (8u << 20)
+wa_status wa_select_pages_noalloc(const wa_layout *layout, const void *q, int32_t n_q,
+                                  const double *page_means, const int32_t *cand, int32_t n_cand,
+                                  const wa_prompt_stage *prompt, int32_t k_p, int32_t *out_idx,
+                                  double *out_scores, void *stream);
+
+/*
  * Sliding window plus selective fetch (Inferix summary, "Dual access
  * patterns": a range of the most recent blocks attended densely, and
  * specific distant blocks fetched by index for long-range context; the

@@ -27,7 +27,7 @@ __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "W
            "wa_block_attention", "wa_paged_attention", "hsa_shape", "wa_hsa_workspace_bytes",
            "wa_hsa_select", "wa_sparse_workspace_bytes", "wa_sparse_attention",
            "wa_page_in", "wa_page_out", "wa_merge_attention", "wa_status_string",
-           "use_library"]
+           "use_library", "wa_select_pages_noalloc"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
 WA_F32, WA_BF16 = 0, 1
@@ -107,6 +107,8 @@ def load_library():
     lib.wa_select_workspace_bytes.restype = sz
     lib.wa_select_pages.argtypes = [L, p, i32, p, p, i32, P, i32, p, p, p, sz, p]
     lib.wa_select_pages.restype = i32
+    lib.wa_select_pages_noalloc.argtypes = [L, p, i32, p, p, i32, P, i32, p, p, p]
+    lib.wa_select_pages_noalloc.restype = i32
     lib.wa_select_window.argtypes = [L, p, i32, p, p, i32, P, p, i32, i32, p, p, p, sz, p]
     lib.wa_select_window.restype = i32
     lib.wa_gather.argtypes = [L, p, p, p, i32, p, p, p]
@@ -282,10 +284,17 @@ def _select(L, q, page_means, k_p, cand, n_cand, prompt, recent, out_idx, out_sc
     _need(out_idx, "out_idx", torch.int32, n_out)
     if out_scores is not None:
         _need(out_scores, "out_scores", torch.float64, n_cand)
+    pst = ctypes.byref(ps) if ps is not None else None
+    if where == "wa_select_pages_noalloc":
+        # the library's own fixed workspace: nothing allocated here or there
+        st = lib.wa_select_pages_noalloc(ctypes.byref(L), _ptr(q), int(n_q), _ptr(page_means),
+                                         _ptr(cand), int(n_cand), pst, int(k_p), _ptr(out_idx),
+                                         _ptr(out_scores), _stream(stream))
+        _check(st, where)
+        return out_idx
     nbytes = lib.wa_select_workspace_bytes(ctypes.byref(L), int(n_q), int(n_cand),
                                            ctypes.byref(ps) if ps is not None else None)
     ws = _workspace(nbytes, workspace, q)
-    pst = ctypes.byref(ps) if ps is not None else None
     if where == "wa_select_pages":
         st = lib.wa_select_pages(ctypes.byref(L), _ptr(q), int(n_q), _ptr(page_means), _ptr(cand),
                                  int(n_cand), pst, int(k_p), _ptr(out_idx), _ptr(out_scores),
@@ -304,6 +313,14 @@ def wa_select_pages(L: Layout, q, page_means, k_p: int, cand=None, n_cand=None, 
     """Top-K_p page ids (device int32 [k_p]) for the chunk's queries q [n_q, H, d]."""
     return _select(L, q, page_means, k_p, cand, n_cand, prompt, None, out_idx, out_scores,
                    workspace, stream, "wa_select_pages")
+
+
+def wa_select_pages_noalloc(L: Layout, q, page_means, k_p: int, cand=None, n_cand=None,
+                            prompt=None, out_idx=None, out_scores=None, stream=None):
+    """wa_select_pages with the library's fixed per-device workspace (no
+    allocation when out_idx is given)."""
+    return _select(L, q, page_means, k_p, cand, n_cand, prompt, None, out_idx, out_scores,
+                   None, stream, "wa_select_pages_noalloc")
 
 
 def wa_select_window(L: Layout, q, page_means, recent, k_p: int, cand=None, n_cand=None,

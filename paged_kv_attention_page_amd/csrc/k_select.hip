@@ -25,10 +25,40 @@
 // invalidate plus the counter's round trip cost more than a boundary.
 #include <math.h>
 
+#include <mutex>
+
 #include "colsum.h"
 #include "wa_internal.h"
 
 namespace wa {
+
+// Workspace of wa_select_pages_noalloc: one fixed array per device, in the
+// library's device image, for callers that cannot allocate.  Every call on a
+// device shares it (calls that overlap on one device race); the selection
+// writes every entry it reads, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[WA_SELECT_NOALLOC_MAX_WORKSPACE];
+
+static constexpr int kMaxDevices = 64;
+
+hipError_t select_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // the array's name is a host-side stand-in: the device address of this
+        // device's copy comes from the runtime, with the device current
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 static constexpr int kGroupCols = 64;     // columns per stage-2 block
 static constexpr int kStage2Threads = 1024;

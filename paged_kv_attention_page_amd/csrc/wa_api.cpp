@@ -79,6 +79,24 @@ size_t wa_select_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_cand
 
 namespace {
 
+// Argument checks of a selection, everything but the workspace.
+wa_status select_check(const wa_layout *L, const void *q, int32_t n_q, const double *page_means,
+                       const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
+                       const int32_t *recent, int32_t n_recent, int32_t k_p, int32_t *out_idx,
+                       double *out_scores) {
+    wa_status st = check_layout(L, true);
+    if (st != WA_OK) return st;
+    if (!q || !page_means || !out_idx) return WA_ERR_INVALID_ARG;
+    if (n_q < 1 || n_cand < 1 || k_p < 0 || k_p > n_cand) return WA_ERR_INVALID_ARG;
+    if (n_recent < 0 || n_recent + k_p < 1 || (n_recent > 0 && !recent)) return WA_ERR_INVALID_ARG;
+    if (n_cand > WA_MAX_CANDIDATES || n_recent > WA_MAX_WINDOW) return WA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(page_means) || !aligned16(out_idx) ||
+        (cand && !aligned16(cand)) || (out_scores && !aligned16(out_scores)) ||
+        ((uintptr_t)recent & 3u))
+        return WA_ERR_INVALID_ARG;
+    return check_prompt(L, prompt, cand, n_cand);
+}
+
 // Shared by wa_select_pages (no window) and wa_select_window.
 wa_status select_impl(const wa_layout *L, const void *q, int32_t n_q, const double *page_means,
                       const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
@@ -112,6 +130,23 @@ wa_status wa_select_pages(const wa_layout *L, const void *q, int32_t n_q, const 
     if (k_p < 1) return WA_ERR_INVALID_ARG;
     return select_impl(L, q, n_q, page_means, cand, n_cand, prompt, nullptr, 0, k_p, out_idx,
                        out_scores, workspace, workspace_bytes, stream);
+}
+
+wa_status wa_select_pages_noalloc(const wa_layout *L, const void *q, int32_t n_q,
+                                  const double *page_means, const int32_t *cand, int32_t n_cand,
+                                  const wa_prompt_stage *prompt, int32_t k_p, int32_t *out_idx,
+                                  double *out_scores, void *stream) {
+    if (k_p < 1) return WA_ERR_INVALID_ARG;
+    wa_status st = select_check(L, q, n_q, page_means, cand, n_cand, prompt, nullptr, 0, k_p,
+                                out_idx, out_scores);
+    if (st != WA_OK) return st;
+    const size_t need = wa_select_workspace_bytes(L, n_q, n_cand, prompt);
+    if (need == 0) return WA_ERR_INVALID_ARG;
+    if (need > WA_SELECT_NOALLOC_MAX_WORKSPACE) return WA_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if (select_scratch(&ws) != hipSuccess) return WA_ERR_HIP;
+    return select_impl(L, q, n_q, page_means, cand, n_cand, prompt, nullptr, 0, k_p, out_idx,
+                       out_scores, ws, need, stream);
 }
 
 wa_status wa_select_window(const wa_layout *L, const void *q, int32_t n_q,

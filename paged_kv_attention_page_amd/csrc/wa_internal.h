@@ -52,6 +52,10 @@ struct SelectWs {
 };
 SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
                           int32_t n_chunks);
+// Device address of this device's fixed selection workspace (the `scratch`
+// array of k_select.hip, WA_SELECT_NOALLOC_MAX_WORKSPACE bytes), looked up
+// once per device; allocates nothing.
+hipError_t select_scratch(void **out);
 
 // ---------------------------------------------------------------------------
 // launchers (return hipSuccess or the launch error)

@@ -152,6 +152,35 @@ def test_select_rejects(lib):
     assert _select(lib, lay=L(pages=0)) == E
 
 
+def _select_noalloc(lib, lay=None, q=A, n_q=100, means=A, cand=NULL, n_cand=16, prompt=None,
+                    k_p=4, out=A):
+    return lib.wa_select_pages_noalloc(lay if lay is not None else L(), q, n_q, means, cand,
+                                       n_cand, prompt, k_p, out, None, None)
+
+
+def test_select_noalloc_rejects_before_touching_the_gpu(lib):
+    """wa_select_pages_noalloc: the same argument rules as wa_select_pages, and
+    a selection whose workspace would exceed the library's fixed per-device
+    array (WA_SELECT_NOALLOC_MAX_WORKSPACE) is refused; all of it before any
+    HIP call."""
+    E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
+    assert _select_noalloc(lib, q=NULL) == E
+    assert _select_noalloc(lib, means=NULL) == E
+    assert _select_noalloc(lib, out=NULL) == E
+    assert _select_noalloc(lib, n_q=0) == E
+    assert _select_noalloc(lib, k_p=0) == E
+    assert _select_noalloc(lib, k_p=17) == E
+    assert _select_noalloc(lib, n_cand=5000, k_p=4) == U
+    assert _select_noalloc(lib, q=MIS) == E
+    assert _select_noalloc(lib, lay=L(pages=0)) == E
+    # workspace of 12 x 128 bf16 rows: fits up to a few hundred thousand queries
+    limit = 8 << 20
+    assert lib.wa_select_workspace_bytes(L(), 4680, 16, None) <= limit
+    big = 1 << 20
+    assert lib.wa_select_workspace_bytes(L(), big, 16, None) > limit
+    assert _select_noalloc(lib, n_q=big) == U
+
+
 def _window(lib, lay=None, q=A, n_q=100, means=A, cand=NULL, n_cand=16, recent=B, n_recent=2,
             k_p=4, out=A, ws=A, wsb=1 << 40):
     return lib.wa_select_window(lay if lay is not None else L(), q, n_q, means, cand, n_cand,
