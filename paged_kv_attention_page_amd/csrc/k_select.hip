@@ -304,8 +304,21 @@ __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
         if (mine) {
             const double s = sc[t];
             const int id = ids[t];
-            int rank = 0;
-            for (int i = 0; i < n_cand; ++i) rank += ranks_before(sc[i], ids[i], i, s, id, t);
+            // 8 candidates' LDS reads in flight at a time (a long list is
+            // otherwise one LDS round trip per candidate)
+            int rank = 0, i = 0;
+            for (; i + 8 <= n_cand; i += 8) {
+                double si[8];
+                int ii[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    si[u] = sc[i + u];
+                    ii[u] = ids[i + u];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) rank += ranks_before(si[u], ii[u], i + u, s, id, t);
+            }
+            for (; i < n_cand; ++i) rank += ranks_before(sc[i], ids[i], i, s, id, t);
             if (rank < k_p) out_idx[rank] = id;
         }
         for (int r = n_valid + t; r < k_p; r += blockDim.x) out_idx[r] = -1;
