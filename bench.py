@@ -175,7 +175,7 @@ def main():
     q, k_own, v_own = up(q_h), up(ko_h), up(vo_h)
     cand = torch.arange(wl.n_pages, dtype=torch.int32, device=dev)
     idx = torch.empty(wl.k_p, dtype=torch.int32, device=dev)
-    ws_sel = torch.empty(wa.wa_select_workspace_bytes(L, wl.n_q, wl.n_pages), dtype=torch.uint8,
+    ws_sel = torch.zeros(wa.wa_select_workspace_bytes(L, wl.n_q, wl.n_pages), dtype=torch.uint8,
                          device=dev)
     ws_attn = torch.empty(max(16, wa.wa_attention_workspace_bytes(L, wl.n_q, wl.n_ctx, wl.n_q)),
                           dtype=torch.uint8, device=dev)
@@ -449,7 +449,7 @@ def bench_chunks(args):
            for c in range(n_chunks)]
     idx = torch.empty(wl.k_p, dtype=torch.int32, device=dev)
     max_cand = wl.n_pages + (n_chunks - 1) * wl.appended_per_chunk
-    ws_sel = torch.empty(wa.wa_select_workspace_bytes(L, wl.n_q, max_cand), dtype=torch.uint8,
+    ws_sel = torch.zeros(wa.wa_select_workspace_bytes(L, wl.n_q, max_cand), dtype=torch.uint8,
                          device=dev)
     ws_attn = torch.empty(max(16, wa.wa_attention_workspace_bytes(L, wl.n_q, wl.n_ctx, wl.n_q)),
                           dtype=torch.uint8, device=dev)

@@ -153,7 +153,10 @@ wa_status wa_append_page(const wa_layout *layout, const void *k_src, const void 
 
 /*
  * Bytes of device workspace wa_select_pages needs (0 if the arguments are
- * invalid).  prompt may be NULL.  Contents need no initialisation.
+ * invalid).  prompt may be NULL.  The workspace must be zero-filled before
+ * its first use (it holds a completion counter); every call leaves it
+ * zero-filled where that matters again, so one workspace serves any number
+ * of calls ordered on one stream.  Calls that overlap on one workspace race.
  */
 size_t wa_select_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n_cand,
                                  const wa_prompt_stage *prompt);

@@ -294,6 +294,9 @@ def _select(L, q, page_means, k_p, cand, n_cand, prompt, recent, out_idx, out_sc
         return out_idx
     nbytes = lib.wa_select_workspace_bytes(ctypes.byref(L), int(n_q), int(n_cand),
                                            ctypes.byref(ps) if ps is not None else None)
+    if workspace is None:
+        # zero-filled before its first use; every call leaves it so again
+        workspace = torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=q.device)
     ws = _workspace(nbytes, workspace, q)
     if where == "wa_select_pages":
         st = lib.wa_select_pages(ctypes.byref(L), _ptr(q), int(n_q), _ptr(page_means), _ptr(cand),

@@ -57,16 +57,20 @@ __device__ __forceinline__ void accumulate_vec(double *acc, uint4 v) {
 //   y      [rows][chunks] vectors copied to y_dst (not summed), or null
 //   lds    row_lanes * group_chunks * VEC doubles of shared memory
 //   part   this row block's partial row ([hd] doubles); the block writes the
-//          columns of its group
+//          columns of its group.  part_col0: the column part[0] stands for (0
+//          for a whole row; the group's first column when part holds only the
+//          group's columns, e.g. in shared memory)
 // Thread t owns vector c0 + t % group_chunks and rows r0 + t / group_chunks,
 // stepping by row_lanes, and accumulates in row order; the row_lanes partials
-// of a column are then added in lane order.
-template <bool BF16>
+// of a column are then added in lane order.  BATCH rows of each thread are
+// in flight together.
+template <bool BF16, int BATCH = 4>
 __device__ __forceinline__ void colsum_block(const uint4 *__restrict__ x, uint4 *__restrict__ x_dst,
                                              const uint4 *__restrict__ y, uint4 *__restrict__ y_dst,
                                              int64_t rows, int chunks, int c0, int group_chunks,
                                              int row_lanes, int rows_per_block, int row_block,
-                                             double *lds, double *__restrict__ part) {
+                                             double *lds, double *__restrict__ part,
+                                             int part_col0 = 0) {
     constexpr int VEC = BF16 ? 8 : 4;
     const int t = threadIdx.x;
     const int gw = min(group_chunks, chunks - c0) * VEC;   // columns in this group
@@ -81,17 +85,17 @@ __device__ __forceinline__ void colsum_block(const uint4 *__restrict__ x, uint4 
     if (lane < row_lanes && c0 + cl < chunks) {
         const int c = c0 + cl;
         int64_t r = r0 + lane;
-        // four rows in flight per thread
-        for (; r + 3 * row_lanes < r1; r += 4 * row_lanes) {
-            uint4 xv[4], yv[4];
+        for (; r + (BATCH - 1) * row_lanes < r1; r += BATCH * row_lanes) {
+            uint4 xv[BATCH], yv[BATCH];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) xv[u] = stream_load(x + (r + u * row_lanes) * chunks + c);
+            for (int u = 0; u < BATCH; ++u) xv[u] = stream_load(x + (r + u * row_lanes) * chunks + c);
             if (y) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) yv[u] = stream_load(y + (r + u * row_lanes) * chunks + c);
+                for (int u = 0; u < BATCH; ++u)
+                    yv[u] = stream_load(y + (r + u * row_lanes) * chunks + c);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < BATCH; ++u) {
                 if (x_dst) stream_store(x_dst + (r + u * row_lanes) * chunks + c, xv[u]);
                 if (y) stream_store(y_dst + (r + u * row_lanes) * chunks + c, yv[u]);
                 accumulate_vec<BF16>(acc, xv[u]);
@@ -110,7 +114,7 @@ __device__ __forceinline__ void colsum_block(const uint4 *__restrict__ x, uint4 
     for (int col = t; col < gw; col += blockDim.x) {
         double s = 0.0;
         for (int ln = 0; ln < row_lanes; ++ln) s += lds[ln * gw + col];
-        part[c0 * VEC + col] = s;
+        part[c0 * VEC - part_col0 + col] = s;
     }
 }
 

@@ -7,7 +7,13 @@
 // so the selection is decided in the same precision as the fp64 reference,
 // and repeated calls are bitwise equal.
 //
-// Three launches, no host synchronisation:
+// Without a prompt stage and with at most kFusedMaxCand candidates: one
+// launch.  Block (column group, row block) forms the fp64 column sums of its
+// rows of Q and, since alpha is linear in qbar, each candidate's dot product
+// with them over the group's columns; the block that finishes last (a
+// completion counter) adds the block partials of each candidate in block
+// order, scales, ranks and writes the result, then clears the counter.
+// Otherwise three launches, no host synchronisation:
 //   stage 1  blocks (column group, row block): fp64 partial column sums of Q
 //            (HBM stream); then one block per past chunk: cosine of the
 //            current prompt with that chunk's prompt (prompt stage only).
@@ -16,13 +22,14 @@
 //            (prompt stage: rank the chunks), and write each candidate's
 //            partial dot product over those columns.
 //   stage 3  one block: alpha_j = the column-group partials of candidate j
-//            added in group order, scaled; then the top K_p.  Up to
-//            blockDim.x candidates, each thread counts the candidates that
-//            rank before its own (one pass, no shuffles); beyond that, K_p
-//            rounds of a wavefront-shuffle argmax.
-// A kernel boundary, not a device-scope fence and counter, hands data from
-// one stage to the next: with one L2 per XCD, the fence's L2 write-back and
-// invalidate plus the counter's round trip cost more than a boundary.
+//            added in group order, scaled; then the top K_p.
+// Ranking (both paths): up to one candidate per thread, each thread counts the
+// candidates that rank before its own (one pass, no shuffles); beyond that,
+// K_p rounds of a wavefront-shuffle argmax.
+// The one-launch path hands its partials over with agent-scope atomic stores
+// and loads (written through to, and read from, the device's coherent level,
+// so no L2 write-back or invalidate is needed), ordered by waiting for the
+// stores before the counter's increment.
 #include <math.h>
 
 #include <mutex>
@@ -64,13 +71,32 @@ static constexpr int kGroupCols = 64;     // columns per stage-2 block
 static constexpr int kStage2Threads = 1024;
 static constexpr int kStage3Threads = 1024;
 static constexpr int kQRowsPerLane = 8;   // rows each stage-1 lane adds
+static constexpr int kFusedMaxCand = 64;  // candidates of the one-launch path
+static constexpr int kFusedRowsPerLane = 16;
+static constexpr int kFusedBatch = 16;      // rows of a lane in flight together
+
+static bool select_one_launch(int32_t n_cand, int32_t n_chunks) {
+    return n_chunks == 0 && n_cand <= kFusedMaxCand;
+}
 
 SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
                           int32_t n_chunks) {
     SelectWs w;
+    // [0, 256): the one-launch path's completion counter, zero between calls;
+    // the three-launch path leaves it alone
+    size_t off = 256;
+    w.one_launch = select_one_launch(n_cand, n_chunks);
+    if (w.one_launch) {
+        w.q_plan = colsum_plan(dtype, hd, n_q, kFusedRowsPerLane);
+        w.groups = w.q_plan.groups;
+        w.alpha_part = off;   // [groups * row blocks][n_cand]
+        off = align_up(off + (size_t)w.q_plan.groups * w.q_plan.blocks * n_cand * sizeof(double), 256);
+        w.partial_q = w.cosine = w.cand = 0;
+        w.total = off;
+        return w;
+    }
     w.q_plan = colsum_plan(dtype, hd, n_q, kQRowsPerLane);
     w.groups = (int)((hd + kGroupCols - 1) / kGroupCols);
-    size_t off = 0;
     w.partial_q = off;
     off = align_up(off + (size_t)w.q_plan.blocks * hd * sizeof(double), 256);
     w.cosine = off;
@@ -252,43 +278,39 @@ __global__ __launch_bounds__(kStage2Threads) void k_select_stage2(const double *
 
 }
 
-// One block of kStage3Threads threads.  With a sliding window (n_recent > 0,
+// The scores of the candidates and their ranking, run by every thread of one
+// block: alpha_of(j) gives candidate j's unscaled score (a sum in a fixed
+// order), id_of(j) its page id.  With a sliding window (n_recent > 0,
 // Inferix summary, "Dual access patterns": range access to the most recent
 // pages plus index-based selective fetch), the window's ids are written
 // first and take no part in the ranking, which fills the k_p entries after
-// them; their scores are still reported.
-__global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
-    const double *__restrict__ alpha_part, int groups, int n_cand,
-    const int32_t *__restrict__ cand_ws, int max_pages, double sqrt_d, int k_p,
-    const int32_t *__restrict__ recent, int n_recent,
-    int32_t *__restrict__ out_idx, double *__restrict__ out_scores) {
-    __shared__ double sc[WA_MAX_CANDIDATES];
-    __shared__ int ids[WA_MAX_CANDIDATES];
+// them; their scores are still reported.  MAXC >= n_cand.
+// NT: the block's thread count.  (The block size is a template argument, not
+// blockDim: reading it, or __syncthreads_count, fetches the launch's size
+// from memory on the critical path.)
+template <int NT, int MAXC, class AlphaOf, class IdOf>
+__device__ void finish_select(AlphaOf alpha_of, IdOf id_of, int n_cand, int max_pages,
+                              double denom, int k_p, const int32_t *__restrict__ recent,
+                              int n_recent, int32_t *__restrict__ out_idx,
+                              double *__restrict__ out_scores) {
+    __shared__ double sc[MAXC];
+    __shared__ int ids[MAXC];
     __shared__ int win[WA_MAX_WINDOW];
+    __shared__ int wave_count[NT / 64];
     const int t = threadIdx.x;
-    for (int r = t; r < n_recent; r += blockDim.x) {
+    for (int r = t; r < n_recent; r += NT) {
         const int id = recent[r];
         win[r] = id;
         out_idx[r] = id;
     }
     __syncthreads();
     out_idx += n_recent;
-    // alpha_j: group partials added in group order; an id outside the pool
-    // scores -inf and is never selected
-    for (int j = t; j < n_cand; j += blockDim.x) {
-        double v = 0.0;
-        for (int g0 = 0; g0 < groups; g0 += 16) {
-            double x[16];   // 16 loads in flight, then added in group order
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                x[u] = g0 + u < groups ? alpha_part[(int64_t)(g0 + u) * n_cand + j] : 0.0;
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (g0 + u < groups) v += x[u];
-        }
-        const int id = cand_ws[j];
+    // an id outside the pool scores -inf and is never selected
+    for (int j = t; j < n_cand; j += NT) {
+        const double v = alpha_of(j);
+        const int id = id_of(j);
         const bool valid = id >= 0 && id < max_pages;
-        const double s = valid ? v / sqrt_d : -INFINITY;
+        const double s = valid ? v / denom : -INFINITY;
         bool in_window = false;
         for (int w = 0; w < n_recent; ++w) in_window |= win[w] == id;
         sc[j] = s;
@@ -297,10 +319,15 @@ __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
     }
     __syncthreads();
 
-    if (n_cand <= (int)blockDim.x) {
+    if (n_cand <= NT) {
         // rank of candidate t = number of candidates ordered before it
         const bool mine = t < n_cand && ids[t] >= 0;
-        const int n_valid = __syncthreads_count(mine);
+        const unsigned long long ballot = __builtin_amdgcn_ballot_w64(mine);
+        if ((t & 63) == 0) wave_count[t >> 6] = __builtin_popcountll(ballot);
+        __syncthreads();
+        int n_valid = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) n_valid += wave_count[w];
         if (mine) {
             const double s = sc[t];
             const int id = ids[t];
@@ -321,7 +348,7 @@ __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
             for (; i < n_cand; ++i) rank += ranks_before(sc[i], ids[i], i, s, id, t);
             if (rank < k_p) out_idx[rank] = id;
         }
-        for (int r = n_valid + t; r < k_p; r += blockDim.x) out_idx[r] = -1;
+        for (int r = n_valid + t; r < k_p; r += NT) out_idx[r] = -1;
         return;
     }
 
@@ -353,6 +380,130 @@ __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
     }
 }
 
+// One block of kStage3Threads threads: alpha_j = the group partials of
+// candidate j added in group order.
+__global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
+    const double *__restrict__ alpha_part, int groups, int n_cand,
+    const int32_t *__restrict__ cand_ws, int max_pages, double sqrt_d, int k_p,
+    const int32_t *__restrict__ recent, int n_recent,
+    int32_t *__restrict__ out_idx, double *__restrict__ out_scores) {
+    auto alpha_of = [&](int j) -> double {
+        double v = 0.0;
+        for (int g0 = 0; g0 < groups; g0 += 16) {
+            double x[16];   // 16 loads in flight, then added in group order
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                x[u] = g0 + u < groups ? alpha_part[(int64_t)(g0 + u) * n_cand + j] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (g0 + u < groups) v += x[u];
+        }
+        return v;
+    };
+    auto id_of = [&](int j) -> int { return cand_ws[j]; };
+    finish_select<kStage3Threads, WA_MAX_CANDIDATES>(alpha_of, id_of, n_cand, max_pages, sqrt_d,
+                                                     k_p, recent, n_recent, out_idx, out_scores);
+}
+
+// The one-launch path: kFusedThreads threads per block, block b -> (column
+// group b % groups, row block b / groups), `blocks` = groups * row blocks.
+static constexpr int kFusedThreads = 256;
+template <bool BF16>
+__global__ __launch_bounds__(kFusedThreads) void k_select_one(
+    const uint4 *__restrict__ q, int64_t n_q, int chunks, int group_chunks, int groups,
+    int row_lanes, int rows_per_block, int blocks, const double *__restrict__ page_means,
+    int64_t hd, int max_pages, const int32_t *__restrict__ cand_in, int n_cand, double denom, int k_p,
+    const int32_t *__restrict__ recent, int n_recent, int *__restrict__ counter,
+    double *__restrict__ alpha_blk, int32_t *__restrict__ out_idx,
+    double *__restrict__ out_scores) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    __shared__ double lds[kFusedThreads * VEC];   // row-lane partials of colsum_block
+    __shared__ double colsum[64 * VEC];           // this block's column sums
+    __shared__ double alpha[kFusedThreads];
+    __shared__ int last;
+    const int t = threadIdx.x, b = blockIdx.x;
+    const int g = b % groups, rb = b / groups;
+    const int c0 = g * group_chunks;
+    const int gw = min(group_chunks, chunks - c0) * VEC;   // columns in this group
+    colsum_block<BF16, kFusedBatch>(q, nullptr, nullptr, nullptr, n_q, chunks, c0, group_chunks,
+                                    row_lanes, rows_per_block, rb, lds, colsum, c0 * VEC);
+    __syncthreads();
+
+    // candidate j's dot product with this block's column sums: tpc = 256 / ncp
+    // consecutive lanes per candidate (ncp = n_cand rounded up to a power of
+    // two, at least 4); lane sub adds columns sub, sub + tpc, ... in order,
+    // 8 loads in flight at a time, then a butterfly over the tpc lanes
+    int ncp = 4;
+    while (ncp < n_cand) ncp <<= 1;
+    const int tpc = kFusedThreads / ncp;
+    {
+        const int j = t / tpc, sub = t % tpc;
+        const int id = j < n_cand ? (cand_in ? cand_in[j] : j) : -1;
+        double v = 0.0;
+        if (id >= 0 && id < max_pages) {
+            const double *pm = page_means + (int64_t)id * hd + (int64_t)c0 * VEC;
+            int c = sub;
+            for (; c + 7 * tpc < gw; c += 8 * tpc) {
+                double x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = pm[c + u * tpc];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v += colsum[c + u * tpc] * x[u];
+            }
+            for (; c < gw; c += tpc) v += colsum[c] * pm[c];
+        }
+        for (int off = tpc >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (sub == 0 && j < n_cand)
+            __hip_atomic_store(alpha_blk + (int64_t)b * n_cand + j, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // this wavefront's stores have reached the coherent level; once every
+    // wavefront is past the barrier, the block counts itself done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0)
+        last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               blocks - 1;
+    __syncthreads();
+    if (!last) return;
+
+    // the last block: alpha_j = block partials of candidate j added in block
+    // order (slice sl of the kFusedThreads / ncp slices adds blocks sl,
+    // sl + slices, ...; then the slices in order)
+    const int slices = kFusedThreads / ncp;
+    {
+        const int j = t % ncp, sl = t / ncp;
+        double v = 0.0;
+        if (j < n_cand) {
+            int bb = sl;
+            for (; bb + 7 * slices < blocks; bb += 8 * slices) {
+                double x[8];   // 8 loads in flight, then added in block order
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    x[u] = __hip_atomic_load(alpha_blk + (int64_t)(bb + u * slices) * n_cand + j,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v += x[u];
+            }
+            for (; bb < blocks; bb += slices)
+                v += __hip_atomic_load(alpha_blk + (int64_t)bb * n_cand + j, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+        alpha[t] = v;   // alpha[sl * ncp + j]
+    }
+    __syncthreads();
+    auto alpha_of = [&](int j) -> double {
+        double v = 0.0;
+        for (int sl = 0; sl < slices; ++sl) v += alpha[sl * ncp + j];
+        return v;
+    };
+    auto id_of = [&](int j) -> int { return cand_in ? cand_in[j] : j; };
+    finish_select<kFusedThreads, kFusedMaxCand>(alpha_of, id_of, n_cand, max_pages, denom, k_p,
+                                                recent, n_recent, out_idx, out_scores);
+    // ready for the next call on this workspace
+    if (t == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const double *page_means,
                          const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
                          const int32_t *recent, int32_t n_recent, int32_t k_p, int32_t *out_idx,
@@ -361,6 +512,21 @@ hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const d
     const int n_chunks = prompt ? prompt->n_chunks : 0;
     const SelectWs w = select_workspace(L.dtype, hd, n_q, n_cand, n_chunks);
     char *base = (char *)ws;
+    if (w.one_launch) {
+        const ColSumPlan &p = w.q_plan;
+        const double denom = (double)n_q * sqrt((double)L.head_dim);
+        auto launch = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(p.groups * p.blocks), dim3(kFusedThreads), 0, s,
+                               (const uint4 *)q, (int64_t)n_q, p.chunks, p.group_chunks, p.groups,
+                               p.row_lanes, p.rows_per_block, p.groups * p.blocks, page_means, hd,
+                               L.max_pages, cand,
+                               n_cand, denom, k_p, recent, n_recent, (int *)base,
+                               (double *)(base + w.alpha_part), out_idx, out_scores);
+        };
+        if (L.dtype == WA_BF16) launch(k_select_one<true>);
+        else launch(k_select_one<false>);
+        return hipGetLastError();
+    }
     double *partial_q = (double *)(base + w.partial_q);
     double *cosine = prompt ? (double *)(base + w.cosine) : nullptr;
     double *alpha_part = (double *)(base + w.alpha_part);

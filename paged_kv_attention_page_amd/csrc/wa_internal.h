@@ -41,7 +41,10 @@ ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lan
 
 size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens);
 
+// Bytes [0, 256) hold the one-launch path's completion counter (zero between
+// calls).  One-launch path: alpha_part is [groups * row blocks][n_cand].
 struct SelectWs {
+    bool one_launch;    // no prompt stage, few candidates: one kernel
     size_t partial_q;   // [q_blocks][hd] double
     size_t cosine;      // [n_chunks] double
     size_t alpha_part;  // [groups][n_cand] double

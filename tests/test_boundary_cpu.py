@@ -176,7 +176,7 @@ def test_select_noalloc_rejects_before_touching_the_gpu(lib):
     # workspace of 12 x 128 bf16 rows: fits up to a few hundred thousand queries
     limit = 8 << 20
     assert lib.wa_select_workspace_bytes(L(), 4680, 16, None) <= limit
-    big = 1 << 20
+    big = 1 << 22
     assert lib.wa_select_workspace_bytes(L(), big, 16, None) > limit
     assert _select_noalloc(lib, n_q=big) == U
 

@@ -308,3 +308,38 @@ def test_prompt_stage_with_zero_norm_prompts(zero):
     assert out_chunks.cpu().numpy().tolist() == ref["chunks"].tolist()
     assert out_cand.cpu().numpy().tolist() == ref["cand"].tolist()
     assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+
+
+def test_select_one_workspace_across_both_paths():
+    """One zero-filled workspace serves a run of selections ordered on one
+    stream: the one-launch path (no prompt stage, at most 64 candidates,
+    whose last block clears the completion counter) and the three-launch
+    path (65 and 70 candidates) in turn, with and without a window, each
+    against the oracle; afterwards the counter is zero again."""
+    wl = W.scaled(W.WORKLOADS["wan_kp4"], name="edge_ws", n_heads=2, frame_tokens=16,
+                  page_frames=2, n_pages=70, chunk_frames=9, k_p=3)   # 32-token pages, 144 queries
+    run = _pool_with_pages(wl, wl.n_pages)
+    q = W.chunk_qkv(wl, 0, 0)[0]
+    qd = to_device(q)
+    host_means = run.oracle_means(range(wl.n_pages))
+    rng = np.random.default_rng(5)
+    cases = [(16, None), (64, None), (65, None), (5, [3, 7]), (70, [1]), (64, [0, 2, 4]),
+             (1, None), (64, None)]
+    nbytes = max(wa.wa_select_workspace_bytes(run.L, q.shape[0], n) for n, _ in cases)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for n_cand, recent in cases:
+        cand = rng.permutation(wl.n_pages)[:n_cand].astype(np.int32)
+        cd = torch.from_numpy(cand).cuda()
+        k_p = min(wl.k_p, n_cand - (len(recent) if recent else 0))
+        say("select one workspace", n_cand, recent)
+        if recent is None:
+            idx = wa.wa_select_pages(run.L, qd, run.means, k_p, cand=cd, workspace=ws)
+            ref = oracle.select_pages(q, host_means, k_p, cand=cand)["idx"]
+        else:
+            rd = torch.tensor(recent, dtype=torch.int32, device="cuda")
+            idx = wa.wa_select_window(run.L, qd, run.means, rd, k_p, cand=cd, workspace=ws)
+            ref = oracle.select_window(q, host_means, k_p, np.array(recent, np.int32),
+                                       cand=cand)["idx"]
+        assert idx.cpu().numpy().tolist() == np.asarray(ref).tolist()
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0
