@@ -331,7 +331,9 @@ def test_hand_written_lists():
 def test_sparse_full_size():
     """wan_kp4 at full size: 4 gathered pages (49,920 keys) + 4,680 own keys,
     12 heads, 4,680 queries (19 query blocks, 464 key blocks); the selection
-    of three query blocks and sampled rows of the output against the oracle."""
+    of three query blocks, and every row of query block 9 and of the ragged
+    last block (72 rows) plus sampled rows of block 0, in both output dtypes,
+    against the oracle."""
     wl = W.WORKLOADS["wan_kp4"]
     q, kc, vc, ko, vo = _inputs(wl, [11, 3, 14, 7], 49920, 4680, gain=8.0)
     tau = [0.5 + 0.04 * h for h in range(wl.n_heads)]
@@ -343,8 +345,8 @@ def test_sparse_full_size():
     torch.cuda.synchronize()
     tiles, count, gini = tiles.cpu().numpy(), count.cpu().numpy(), gini.cpu().numpy()
     q_blocks = wa.hsa_shape(L, q.shape[0], 49920, 4680)[0]
-    rows = np.concatenate([np.arange(0, 256, 51), np.arange(256 * 9, 256 * 10, 51),
-                           np.arange(256 * 18, q.shape[0], 51), [q.shape[0] - 1]])
+    rows = np.concatenate([np.arange(0, 256, 51), np.arange(256 * 9, 256 * 10),
+                           np.arange(256 * 18, q.shape[0])])
     ref = oracle.hsa_sparse(q, kc, vc, ko, vo, wl.softmax_scale, tau, rows=rows)
     blocks = ref["blocks"]
     for (h, b), chosen in ref["sel"].items():
@@ -352,13 +354,14 @@ def test_sparse_full_size():
         _clear_cut(ref["maps"][b][h], tau[h])
         assert tiles[item, :count[item]].tolist() == _tiles_of(blocks, chosen)
         assert abs(gini[item] - ref["gini"][(h, b)]) <= 1e-12
-    say("sparse attention, full size")
-    out = wa.wa_sparse_attention(L, to_device(q), to_device(kc), to_device(vc), to_device(ko),
-                                 to_device(vo), torch.from_numpy(tiles).cuda(),
-                                 torch.from_numpy(count).cuda(), wl.softmax_scale,
-                                 out_dtype=wa.WA_BF16)
-    torch.cuda.synchronize()
-    assert np.abs(to_f64(out)[rows] - ref["out"]).max() <= attention_tolerance(wl)
+    for odt in (wa.WA_BF16, wa.WA_F32):
+        say("sparse attention, full size", odt)
+        out = wa.wa_sparse_attention(L, to_device(q), to_device(kc), to_device(vc),
+                                     to_device(ko), to_device(vo), torch.from_numpy(tiles).cuda(),
+                                     torch.from_numpy(count).cuda(), wl.softmax_scale,
+                                     out_dtype=odt)
+        torch.cuda.synchronize()
+        assert np.abs(to_f64(out)[rows] - ref["out"]).max() <= attention_tolerance(wl)
 
 
 def test_full_size_full_list_does_not_split_and_equals_dense():
