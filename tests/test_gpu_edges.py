@@ -343,3 +343,29 @@ def test_select_one_workspace_across_both_paths():
         assert idx.cpu().numpy().tolist() == np.asarray(ref).tolist()
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("dtype,n_heads,head_dim,n_q,n_pages", [
+    (W.F32, 2, 64, 700, 10),      # fp32: 32 column vectors, one group, 6 row blocks
+    (W.F32, 3, 128, 1500, 9),     # fp32: 96 vectors, two groups (64 + 32)
+    (W.BF16, 3, 64, 1100, 12),    # bf16: 24 vectors, a group narrower than 64
+    (W.BF16, 5, 128, 2000, 40),   # bf16: 80 vectors, two groups (64 + 16); 40 candidates
+], ids=["f32_h2_d64", "f32_h3_d128", "bf16_h3_d64", "bf16_h5_d128_40cand"])
+def test_select_layouts_and_shapes(dtype, n_heads, head_dim, n_q, n_pages):
+    """The one-launch selection over layouts whose column groups are narrower
+    than 64 vectors or ragged, with several row blocks, against the oracle
+    (ids, scores to 1e-12)."""
+    base = W.WORKLOADS["tiny_f32"] if dtype == W.F32 else W.WORKLOADS["wan_kp4"]
+    wl = W.scaled(base, name="sel_%s_%d_%d" % (dtype, n_heads, head_dim), dtype=dtype,
+                  n_heads=n_heads, head_dim=head_dim, frame_tokens=16, page_frames=2,
+                  n_pages=n_pages, chunk_frames=1, k_p=3, scale=head_dim ** -0.5)
+    run = _pool_with_pages(wl, wl.n_pages)
+    rng = np.random.default_rng([n_q, n_pages])
+    q = W.encode(wl, rng.standard_normal((n_q, n_heads, head_dim), dtype=np.float32))
+    scores = torch.empty(n_pages, dtype=torch.float64, device="cuda")
+    say("select layout", dtype, n_heads, head_dim, n_q, n_pages)
+    idx = wa.wa_select_pages(run.L, to_device(q), run.means, wl.k_p, out_scores=scores)
+    ref = oracle.select_pages(q, run.oracle_means(range(n_pages)), wl.k_p)
+    assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+    got = scores.cpu().numpy()
+    assert np.abs(got - ref["alpha"]).max() <= 1e-12 * max(1.0, np.abs(ref["alpha"]).max())
