@@ -13,11 +13,12 @@
 
 namespace wa {
 
-ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lane) {
+ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lane,
+                       int max_group_chunks) {
     ColSumPlan p;
     p.vec = 16 / elem_bytes(dtype);
     p.chunks = (int)(hd / p.vec);
-    p.group_chunks = p.chunks < 64 ? p.chunks : 64;
+    p.group_chunks = p.chunks < max_group_chunks ? p.chunks : max_group_chunks;
     p.groups = (p.chunks + p.group_chunks - 1) / p.group_chunks;
     p.row_lanes = 256 / p.group_chunks;
     p.threads = p.group_chunks * p.row_lanes;
@@ -28,8 +29,11 @@ ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lan
     return p;
 }
 
+// Groups of 32 sixteen-byte vectors (8 row lanes x 8 rows = 64 rows per
+// block): measured 33.2 us per Wan-shaped page against 34.5 us with groups of
+// 64 vectors and 32 rows (and 33.7-37.2 us for 8 or 16 vectors per group).
 static ColSumPlan append_plan(int32_t dtype, int64_t hd, int64_t page_tokens) {
-    return colsum_plan(dtype, hd, page_tokens, 8);
+    return colsum_plan(dtype, hd, page_tokens, 8, 32);
 }
 
 size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens) {

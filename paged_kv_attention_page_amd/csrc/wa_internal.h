@@ -34,7 +34,10 @@ struct ColSumPlan {
     int rows_per_block;
     int blocks;   // row blocks
 };
-ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lane);
+// Column groups of at most max_group_chunks 16-byte vectors (64 fills a
+// 256-thread block with 4 row lanes).
+ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lane,
+                       int max_group_chunks = 64);
 
 // ---------------------------------------------------------------------------
 // workspace layouts
