@@ -175,7 +175,9 @@ size_t wa_select_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n
  * out_idx: device [k_p] int32.  out_scores: device [n_cand] double (alpha in
  * candidate order), or NULL.  A candidate id outside [0, max_pages) is never
  * read: it scores -inf and ranks last; ranks that only such ids could fill
- * get -1.  Duplicate ids are distinct candidates.
+ * get -1.  Duplicate ids are distinct candidates.  workspace: device, >=
+ * wa_select_workspace_bytes(...) bytes, zero-filled before its first use
+ * (see wa_select_workspace_bytes).
  * Errors: NULL layout / q / page_means / out_idx / workspace, n_q < 1,
  * n_cand < 1, k_p < 1 or k_p > n_cand, inconsistent prompt stage, workspace
  * too small -> WA_ERR_INVALID_ARG; n_cand or n_chunks > WA_MAX_CANDIDATES,
