@@ -15,7 +15,8 @@ Inputs are resident in HBM before the timed region.
 Output: one JSON line.  `value` is block-attention TFLOP/s over the whole
 step (attention FLOPs / step time).  Kernel-level figures (attention TFLOP/s
 and its fraction of the bf16 matrix-core peak, select + gather GB/s and its
-fraction of HBM peak) are measured with HIP events on the launch stream.
+fraction of HBM peak) are measured with HIP events on the launch stream
+(timing-only events, recorded without a system-scope fence).
 The CPU baseline is the fp64 oracle timed on a bounded row sample.
 """
 from __future__ import annotations
@@ -34,6 +35,66 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+class TimingEvent:
+    """A HIP event used for timing only, created with hipEventDisableSystemFence.
+
+    A default event performs a system-scope release when it is recorded (a
+    cache write-back and invalidate), which delays the next kernel on the
+    stream by microseconds and so shows up inside the intervals being
+    measured; an event created with this flag skips that fence and records the
+    same end-of-pipe timestamp (HIP runtime API, hipEventCreateWithFlags).
+    Recorded on the stream the kernels are launched on; read after a device
+    synchronisation."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            for name in ("libamdhip64.so.7", "libamdhip64.so"):
+                try:   # the runtime torch and libwa.so already share
+                    lib = ctypes.CDLL(name, mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+                    break
+                except OSError:
+                    continue
+            else:
+                raise RuntimeError("the HIP runtime is not loaded in this process")
+            vp = ctypes.c_void_p
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [vp, vp]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            lib.hipEventDestroy.argtypes = [vp]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._c = ctypes
+        self.hip = self._runtime()
+        self.ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+
+    def record(self, stream):
+        rc = self.hip.hipEventRecord(self.ev, self._c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = self._c.c_float()
+        rc = self.hip.hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "ev", None) and self.hip is not None:
+            self.hip.hipEventDestroy(self.ev)
 
 
 def cold_entry(ms, nbytes):
@@ -226,7 +287,7 @@ def main():
 
     # K timed steps between two synchronisations; HIP events recorded on the
     # launch stream inside the same region give the per-kernel durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     clocks = ClockSampler(getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None))
     clocks.start()
     torch.cuda.synchronize()
@@ -245,7 +306,7 @@ def main():
 
     # split pass (untimed for the step figure): select and gather separately
     n_split = min(args.steps, 10)
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_split)]
+    sev = [[TimingEvent() for _ in range(3)] for _ in range(n_split)]
     for k in range(n_split):
         step(split=sev[k])
     torch.cuda.synchronize()
@@ -260,7 +321,7 @@ def main():
     for k in range(10):
         for name in ("append", "select_gather"):
             flush.fill_(k & 0xff)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = TimingEvent(), TimingEvent()
             e0.record(stream)
             if name == "append":
                 wa.wa_append_page(L, k_new, v_new, k_pool, v_pool, spare, means,
@@ -293,7 +354,7 @@ def main():
     n_paged = args.steps
     for _ in range(5):
         step_paged()
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_paged)]
+    pev = [[TimingEvent() for _ in range(2)] for _ in range(n_paged)]
     torch.cuda.synchronize()
     tp0 = time.perf_counter()
     for k in range(n_paged):
@@ -493,7 +554,7 @@ def bench_chunks(args):
     for w in range(args.warmup):
         chunk(w % n_chunks)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(T + 3)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(T + 3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -595,7 +656,7 @@ def sparse_pass(wa, W, wl, L, up, k_ctx, v_ctx, k_own, v_own, out, stream, steps
 
     for _ in range(5):
         one()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for k in range(steps):
         one(evs[k])
@@ -604,7 +665,7 @@ def sparse_pass(wa, W, wl, L, up, k_ctx, v_ctx, k_own, v_own, out, stream, steps
     att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     # a chunk's later denoising steps: same context, so the selection takes
     # the context block sums the calls above left in ws
-    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    rev = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
     for k in range(steps):
         rev[k][0].record(stream)
         wa.wa_hsa_select(L, q_sp, k_ctx, k_own, tau, scale=wl.softmax_scale, sel_tiles=tiles,
@@ -686,7 +747,7 @@ def tier_pass(wa, wl, L, k_pool, v_pool, q, k_own, v_own, idx, spare, stream, re
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(st)
         for _ in range(reps):
             fn()

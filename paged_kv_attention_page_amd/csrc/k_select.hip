@@ -23,9 +23,10 @@
 //            partial dot product over those columns.
 //   stage 3  one block: alpha_j = the column-group partials of candidate j
 //            added in group order, scaled; then the top K_p.
-// Ranking (both paths): up to one candidate per thread, each thread counts the
-// candidates that rank before its own (one pass, no shuffles); beyond that,
-// K_p rounds of a wavefront-shuffle argmax.
+// Ranking (both paths): with at most one candidate per thread, a candidate's
+// rank (the number of candidates ordered before it) is counted by a group of
+// lanes, each comparing a share of the list, and summed over the group; beyond
+// that, K_p rounds of a wavefront-shuffle argmax.
 // The one-launch path hands its partials over with agent-scope atomic stores
 // and loads (written through to, and read from, the device's coherent level,
 // so no L2 write-back or invalidate is needed), ordered by waiting for the
@@ -74,6 +75,12 @@ static constexpr int kQRowsPerLane = 8;   // rows each stage-1 lane adds
 static constexpr int kFusedMaxCand = 64;  // candidates of the one-launch path
 static constexpr int kFusedRowsPerLane = 16;
 static constexpr int kFusedBatch = 16;      // rows of a lane in flight together
+// One-launch column groups of 16 sixteen-byte vectors (x 256 rows per block):
+// each block then reads a quarter of the page-mean bytes that groups of 64
+// vectors need.  On a 4,680 x 1,536 bf16 chunk: 10.9-11.3 us with groups of
+// 16, 32 or 64 vectors at 16 candidates, but 14.4 us against 16.0 (32) and
+// 17.0 us (64) at 48 candidates.
+static constexpr int kFusedGroupChunks = 16;
 
 static bool select_one_launch(int32_t n_cand, int32_t n_chunks) {
     return n_chunks == 0 && n_cand <= kFusedMaxCand;
@@ -87,7 +94,7 @@ SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand
     size_t off = 256;
     w.one_launch = select_one_launch(n_cand, n_chunks);
     if (w.one_launch) {
-        w.q_plan = colsum_plan(dtype, hd, n_q, kFusedRowsPerLane);
+        w.q_plan = colsum_plan(dtype, hd, n_q, kFusedRowsPerLane, kFusedGroupChunks);
         w.groups = w.q_plan.groups;
         w.alpha_part = off;   // [groups * row blocks][n_cand]
         off = align_up(off + (size_t)w.q_plan.groups * w.q_plan.blocks * n_cand * sizeof(double), 256);
@@ -113,9 +120,8 @@ SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand
 // ascending, then list position ascending (a repeated id is taken once per
 // occurrence, in list order).  An id < 0 marks "no item" and ranks last.
 __device__ __forceinline__ bool ranks_before(double sa, int ia, int ja, double sb, int ib, int jb) {
-    if (ib < 0) return ia >= 0;
-    if (ia < 0) return false;
-    return sa > sb || (sa == sb && (ia < ib || (ia == ib && ja < jb)));
+    const bool tie = (sa == sb) & ((ia < ib) | ((ia == ib) & (ja < jb)));
+    return (ia >= 0) & ((ib < 0) | (sa > sb) | tie);
 }
 
 // Butterfly argmax over the 64 lanes of a wavefront; every lane ends with the
@@ -296,7 +302,6 @@ __device__ void finish_select(AlphaOf alpha_of, IdOf id_of, int n_cand, int max_
     __shared__ double sc[MAXC];
     __shared__ int ids[MAXC];
     __shared__ int win[WA_MAX_WINDOW];
-    __shared__ int wave_count[NT / 64];
     const int t = threadIdx.x;
     for (int r = t; r < n_recent; r += NT) {
         const int id = recent[r];
@@ -320,35 +325,34 @@ __device__ void finish_select(AlphaOf alpha_of, IdOf id_of, int n_cand, int max_
     __syncthreads();
 
     if (n_cand <= NT) {
-        // rank of candidate t = number of candidates ordered before it
-        const bool mine = t < n_cand && ids[t] >= 0;
-        const unsigned long long ballot = __builtin_amdgcn_ballot_w64(mine);
-        if ((t & 63) == 0) wave_count[t >> 6] = __builtin_popcountll(ballot);
-        __syncthreads();
-        int n_valid = 0;
-#pragma unroll
-        for (int w = 0; w < NT / 64; ++w) n_valid += wave_count[w];
-        if (mine) {
-            const double s = sc[t];
-            const int id = ids[t];
-            // 8 candidates' LDS reads in flight at a time (a long list is
-            // otherwise one LDS round trip per candidate)
-            int rank = 0, i = 0;
-            for (; i + 8 <= n_cand; i += 8) {
-                double si[8];
-                int ii[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    si[u] = sc[i + u];
-                    ii[u] = ids[i + u];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) rank += ranks_before(si[u], ii[u], i + u, s, id, t);
-            }
-            for (; i < n_cand; ++i) rank += ranks_before(sc[i], ids[i], i, s, id, t);
-            if (rank < k_p) out_idx[rank] = id;
+        // rank of candidate j = number of candidates ordered before it, found
+        // by lpc consecutive lanes (lpc = NT / ncp, at most a wavefront; ncp =
+        // n_cand rounded up to a power of two): lane sub compares candidates
+        // sub, sub + lpc, ... with j, then the lanes' counts are added in a
+        // butterfly (rank in the low 16 bits, valid candidates in the high).
+        // The lanes of candidate 0 fill the places past the valid ones with -1.
+        static_assert((NT & (NT - 1)) == 0, "block size must be a power of two");
+        int sh = 0;                 // ncp = 1 << sh
+        while ((1 << sh) < n_cand) ++sh;
+        constexpr int kLogNT = __builtin_ctz(NT);
+        const int lsh = kLogNT - sh < 6 ? kLogNT - sh : 6;
+        const int lpc = 1 << lsh;
+        const int j = t >> lsh, sub = t & (lpc - 1);
+        const bool live = j < n_cand && ids[j] >= 0;
+        const double s = live ? sc[j] : 0.0;
+        const int id = live ? ids[j] : -1;
+        int x = 0;
+        for (int i = sub; i < n_cand; i += lpc) {
+            const int ii = ids[i];
+            x += (int)ranks_before(sc[i], ii, i, s, id, j) + (ii >= 0 ? 1 << 16 : 0);
         }
-        for (int r = n_valid + t; r < k_p; r += NT) out_idx[r] = -1;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            if (off < lpc) x += __shfl_xor(x, off, 64);
+        const int rank = x & 0xffff, valid = x >> 16;
+        if (sub == 0 && live && rank < k_p) out_idx[rank] = id;
+        if (j == 0)
+            for (int r = valid + sub; r < k_p; r += lpc) out_idx[r] = -1;
         return;
     }
 
@@ -475,19 +479,19 @@ __global__ __launch_bounds__(kFusedThreads) void k_select_one(
         const int j = t % ncp, sl = t / ncp;
         double v = 0.0;
         if (j < n_cand) {
-            int bb = sl;
-            for (; bb + 7 * slices < blocks; bb += 8 * slices) {
-                double x[8];   // 8 loads in flight, then added in block order
+            const int terms = sl < blocks ? (blocks - 1 - sl) / slices + 1 : 0;
+            for (int u0 = 0; u0 < terms; u0 += 16) {
+                double x[16];   // up to 16 loads in flight, then added in block order
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    x[u] = __hip_atomic_load(alpha_blk + (int64_t)(bb + u * slices) * n_cand + j,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int u = 0; u < 16; ++u)
+                    x[u] = u0 + u < terms
+                               ? __hip_atomic_load(alpha_blk + (int64_t)(sl + (u0 + u) * slices) * n_cand + j,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.0;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v += x[u];
+                for (int u = 0; u < 16; ++u)
+                    if (u0 + u < terms) v += x[u];
             }
-            for (; bb < blocks; bb += slices)
-                v += __hip_atomic_load(alpha_blk + (int64_t)bb * n_cand + j, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
         }
         alpha[t] = v;   // alpha[sl * ncp + j]
     }
