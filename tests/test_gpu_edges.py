@@ -217,6 +217,42 @@ def test_select_long_candidate_lists_with_repeats(n_cand, k_p):
     assert idx.cpu().numpy().tolist() == ref + [-1] * (k_p - len(ref))
 
 
+def test_select_exact_ties_between_pages():
+    """Byte-identical pages in several slots have identical mean keys, so their
+    scores tie exactly: the order is then by page id, and a repeated id by
+    list position.  Every rank is checked against the oracle, on the
+    one-launch path (12 candidates), the three-launch path (70 candidates
+    with repeats) and with a window holding one member of a tie group."""
+    wl = W.scaled(BF, name="edge_ties", n_pages=12)
+    run = PoolRun(wl)
+    twins = {6: 3, 9: 3, 10: 1, 11: 7}          # slot -> the page stored there again
+    for s_ in range(wl.n_pages):
+        run.append(twins.get(s_, s_), slot=s_)
+    q = W.chunk_qkv(wl, 0, 0)[0]
+    qd = to_device(q)
+    host_means = run.oracle_means(range(wl.n_pages))
+    means = run.means.cpu().numpy()
+    assert np.array_equal(means[6], means[3]) and np.array_equal(means[10], means[1])
+    rng = np.random.default_rng(5)
+    cases = [("all 12 slots", np.arange(12, dtype=np.int32), 12),
+             ("70 listed", rng.permutation(np.tile(np.arange(12, dtype=np.int32), 6)[:70]).astype(np.int32), 20)]
+    for name, cand, k_p in cases:
+        say("select exact ties:", name)
+        scores = torch.empty(cand.size, dtype=torch.float64, device="cuda")
+        idx = wa.wa_select_pages(run.L, qd, run.means, k_p, cand=torch.from_numpy(cand).cuda(),
+                                 out_scores=scores)
+        ref = oracle.select_pages(q, host_means, k_p, cand=cand)
+        assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+        got = scores.cpu().numpy()
+        assert got[cand == 6][0] == got[cand == 3][0] == got[cand == 9][0]
+        assert np.abs(got - ref["alpha"]).max() <= 1e-12 * max(1.0, np.abs(ref["alpha"]).max())
+    say("select exact ties: window [9]")
+    recent = np.array([9], dtype=np.int32)
+    idx = wa.wa_select_window(run.L, qd, run.means, torch.from_numpy(recent).cuda(), 8)
+    ref = oracle.select_window(q, host_means, 8, recent)
+    assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+
+
 @pytest.mark.parametrize("n_cand", [11, 1031])
 def test_select_fewer_valid_candidates_than_k_p(n_cand):
     wl = BF
