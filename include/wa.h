@@ -43,7 +43,10 @@
  *   - Memory: every array argument is DEVICE memory owned by the caller,
  *     except the wa_layout / wa_prompt_stage structs themselves, which are
  *     host memory read during the call only.  The library allocates and frees
- *     nothing and keeps no global state; calls are reentrant.
+ *     nothing and keeps no global state, with one exception: the fixed
+ *     per-device workspace of wa_select_pages_noalloc (see there).  Calls
+ *     are reentrant, except that wa_select_pages_noalloc calls overlapping
+ *     on one GPU share that workspace.
  *   - Layout: token-major and dense.  A K, V, Q or output array of T tokens
  *     is [T][n_heads][head_dim]; the pool is [max_pages][page_tokens][n_heads]
  *     [head_dim]; page_means is [max_pages][n_heads][head_dim] double.
@@ -143,9 +146,10 @@ size_t wa_append_workspace_bytes(const wa_layout *layout);
  * Any other overlap of source and pool is undefined.  The sum is
  * accumulated in fp64 in a fixed order, so repeated calls are bitwise equal.
  * workspace: device, >= wa_append_workspace_bytes(layout) bytes.
- * Errors: NULL layout / k_src / k_pool / page_means / workspace, slot outside
- * [0, max_pages), workspace too small -> WA_ERR_INVALID_ARG; unsupported
- * layout -> WA_ERR_UNSUPPORTED.
+ * Errors: NULL layout / k_src / k_pool / page_means / workspace, v_src
+ * without v_pool, slot outside [0, max_pages), misaligned pointers,
+ * workspace too small -> WA_ERR_INVALID_ARG; unsupported layout ->
+ * WA_ERR_UNSUPPORTED.
  */
 wa_status wa_append_page(const wa_layout *layout, const void *k_src, const void *v_src,
                          void *k_pool, void *v_pool, int32_t slot, double *page_means,
@@ -179,8 +183,8 @@ size_t wa_select_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_t n
  * wa_select_workspace_bytes(...) bytes, zero-filled before its first use
  * (see wa_select_workspace_bytes).
  * Errors: NULL layout / q / page_means / out_idx / workspace, n_q < 1,
- * n_cand < 1, k_p < 1 or k_p > n_cand, inconsistent prompt stage, workspace
- * too small -> WA_ERR_INVALID_ARG; n_cand or n_chunks > WA_MAX_CANDIDATES,
+ * n_cand < 1, k_p < 1 or k_p > n_cand, inconsistent prompt stage, misaligned
+ * pointers, workspace too small -> WA_ERR_INVALID_ARG; n_cand or n_chunks > WA_MAX_CANDIDATES,
  * unsupported layout -> WA_ERR_UNSUPPORTED.
  */
 wa_status wa_select_pages(const wa_layout *layout, const void *q, int32_t n_q,
@@ -244,7 +248,8 @@ wa_status wa_select_window(const wa_layout *layout, const void *q, int32_t n_q,
  * NULL (K only).  A rank whose idx is outside [0, max_pages) is left
  * unwritten.  The pool and the destination must not overlap.
  * Errors: NULL layout / k_pool / idx / k_ctx, only one of v_pool / v_ctx NULL,
- * k_p < 1 -> WA_ERR_INVALID_ARG; unsupported layout -> WA_ERR_UNSUPPORTED.
+ * k_p < 1, misaligned pointers -> WA_ERR_INVALID_ARG; k_p > 65535,
+ * unsupported layout -> WA_ERR_UNSUPPORTED.
  */
 wa_status wa_gather(const wa_layout *layout, const void *k_pool, const void *v_pool,
                     const int32_t *idx, int32_t k_p, void *k_ctx, void *v_ctx, void *stream);
@@ -279,9 +284,10 @@ wa_status wa_gather(const wa_layout *layout, const void *k_pool, const void *v_p
  * key range of some (query block, head) items over several blocks so that
  * every CU has work, and must not be shared by calls in flight at once.
  * Errors: NULL layout / q / out, NULL pointers of a non-empty segment,
- * n_q < 1, n_ctx < 0, n_own < 0, n_ctx + n_own < 1, non-finite
- * softmax_scale, workspace missing or too small -> WA_ERR_INVALID_ARG;
- * head_dim or out_dtype not supported for the dtype -> WA_ERR_UNSUPPORTED.
+ * n_q < 1, n_ctx < 0, n_own < 0, n_ctx + n_own < 1, softmax_scale not finite
+ * and > 0, misaligned pointers (lse: 4-byte aligned), workspace missing,
+ * misaligned or too small -> WA_ERR_INVALID_ARG; head_dim or out_dtype not
+ * supported for the dtype, n_ctx + n_own > 2^31 - 257 -> WA_ERR_UNSUPPORTED.
  */
 wa_status wa_block_attention(const wa_layout *layout, const void *q, int32_t n_q,
                              const void *k_ctx, const void *v_ctx, int32_t n_ctx,
@@ -313,7 +319,8 @@ size_t wa_attention_workspace_bytes(const wa_layout *layout, int32_t n_q, int32_
  * access leaves it, and the result is then unspecified).  Other arguments,
  * precision, workspace (wa_attention_workspace_bytes with n_ctx =
  * k_p * page_tokens) and errors as wa_block_attention, plus: NULL k_pool /
- * v_pool / idx, k_p < 1, page_tokens or max_pages < 1 -> WA_ERR_INVALID_ARG.
+ * v_pool / idx, idx not 4-byte aligned, k_p < 1, page_tokens or max_pages < 1
+ * -> WA_ERR_INVALID_ARG; k_p * page_tokens > 2^31 - 257 -> WA_ERR_UNSUPPORTED.
  * The fast path reads whole 64-key tiles from one page and needs
  * page_tokens % 64 == 0 (bf16); other page sizes take a slower per-row path.
  */
