@@ -9,6 +9,11 @@ stream.  The functions carry the C names:
   wa_gather           copy the selected pages into one contiguous K/V buffer
   wa_block_attention  unmasked softmax attention over [gathered ++ own] K/V
 
+and the rest of ``wa.h`` under the same names: wa_select_window,
+wa_select_pages_noalloc, wa_paged_attention, wa_hsa_select,
+wa_sparse_attention, wa_page_in, wa_page_out, wa_merge_attention and the
+workspace-size queries.
+
 Host-side shape checks here only make sure every pointer handed to the
 library covers the extent the call will touch.  If ``libwa.so`` has not been
 built, loading fails loudly; there is no fallback path.
