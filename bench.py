@@ -112,9 +112,11 @@ def attention_flops(n_q, n_k, head_dim, n_heads):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--config", default="2", choices=["2", "3", "5", "share"],
+    ap.add_argument("--config", default="2", choices=["2", "3", "4", "5", "share"],
                     help="2: the Wan-shaped K_p=4 step (the headline line); 3: full history "
-                         "(6 pages, all attended, 4 denoising steps per chunk); 5: long horizon "
+                         "(6 pages, all attended, 4 denoising steps per chunk); 4: prompt + page "
+                         "selection (64 pages in 16 chunks, the prompt stage keeps 4 chunks); "
+                         "5: long horizon "
                          "(128 -> 136 resident pages, 8 chunks x 4 steps, one page appended per "
                          "chunk); share: config 2 at 3 heads, one GPU's share of a 4-way "
                          "head-sharded layer")
@@ -198,7 +200,7 @@ def main():
               "share of the work; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    if args.config in ("3", "5"):
+    if args.config in ("3", "4", "5"):
         print(json.dumps(bench_chunks(args)), flush=True)
         return
 
@@ -470,19 +472,25 @@ def roofline_mfma(flops, ms, traffic=None):
 
 
 def bench_chunks(args):
-    """Configs 3 and 5: whole chunks of the block-diffusion cadence (Inferix
+    """Configs 3, 4 and 5: whole chunks of the block-diffusion cadence (Inferix
     summary, section 3.4, Steps 3 and 4): per chunk, select + gather once, then
-    T = 4 denoising steps of attention, each with fresh queries and own K/V
-    over the same gathered pages; config 5 then appends one new page (the
-    pool grows from 128 to 136 pages over 8 chunks).  One timed step = one
-    chunk; `value` = attention FLOPs of the chunk / chunk time."""
+    T denoising steps of attention (4 in configs 3 and 5, 1 in config 4), each
+    with fresh queries and own K/V over the same gathered pages; config 5 then
+    appends one new page (the pool grows from 128 to 136 pages over 8 chunks).
+    Config 4 selects in two stages (WorldAttention review, "HKV: Page-Level
+    Multi-Tier Memory"): the prompt stage keeps the 4 of 16 past chunks whose
+    4,096-dim prompt embeddings are closest in cosine to the current one, and
+    the page stage the top 4 of their 16 pages.  One timed step = one chunk;
+    `value` = attention FLOPs of the chunk / chunk time."""
     import torch
 
     import paged_kv_attention_page_amd as wa
     import wa_workloads as W
 
     long_h = args.config == "5"
-    wl = W.WORKLOADS["long_horizon" if long_h else "full_history"]
+    two_stage = args.config == "4"
+    name = {"3": "full_history", "4": "prompt_page", "5": "long_horizon"}[args.config]
+    wl = W.WORKLOADS[name]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     L = wa.layout(wa.WA_BF16, wl.n_heads, wl.head_dim, wl.page_tokens, wl.max_pages)
@@ -509,16 +517,25 @@ def bench_chunks(args):
     qkv = [[tuple(up(x) for x in W.chunk_qkv(wl, c, t)) for t in range(T)]
            for c in range(n_chunks)]
     idx = torch.empty(wl.k_p, dtype=torch.int32, device=dev)
-    max_cand = wl.n_pages + (n_chunks - 1) * wl.appended_per_chunk
-    ws_sel = torch.zeros(wa.wa_select_workspace_bytes(L, wl.n_q, max_cand), dtype=torch.uint8,
-                         device=dev)
+    prompt = prompt_h = None
+    if two_stage:
+        prompt_h = dict(chunk_prompts=W.chunk_prompts(wl), cur_prompt=W.current_prompt(wl),
+                        chunk_pages=W.chunk_page_map(wl), n_keep=wl.n_cand_groups)
+        prompt = {k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v)
+                  for k, v in prompt_h.items()}
+        max_cand = wl.n_cand_groups * wl.pages_per_group
+    else:
+        max_cand = wl.n_pages + (n_chunks - 1) * wl.appended_per_chunk
+    ws_sel = torch.zeros(wa.wa_select_workspace_bytes(L, wl.n_q, max_cand, prompt),
+                         dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(max(16, wa.wa_attention_workspace_bytes(L, wl.n_q, wl.n_ctx, wl.n_q)),
                           dtype=torch.uint8, device=dev)
     ctx_shape = (wl.n_ctx, wl.n_heads, wl.head_dim)
     k_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
     v_ctx = torch.empty(ctx_shape, dtype=torch.bfloat16, device=dev)
     out = torch.empty((wl.n_q, wl.n_heads, wl.head_dim), dtype=torch.bfloat16, device=dev)
-    cands = [torch.arange(wl.n_pages + c * wl.appended_per_chunk, dtype=torch.int32, device=dev)
+    cands = [None if two_stage else
+             torch.arange(wl.n_pages + c * wl.appended_per_chunk, dtype=torch.int32, device=dev)
              for c in range(n_chunks)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -532,8 +549,8 @@ def bench_chunks(args):
         cand = cands[c]
         if ev is not None:
             ev[0].record(stream)
-        wa.wa_select_pages(L, qkv[c][0][0], means, wl.k_p, cand=cand, out_idx=idx,
-                           workspace=ws_sel, stream=stream)
+        wa.wa_select_pages(L, qkv[c][0][0], means, wl.k_p, cand=cand, prompt=prompt,
+                           out_idx=idx, workspace=ws_sel, stream=stream)
         wa.wa_gather(L, k_pool, v_pool, idx, wl.k_p, k_ctx, v_ctx, stream=stream)
         if ev is not None:
             ev[1].record(stream)
@@ -566,19 +583,31 @@ def bench_chunks(args):
     att = [e[1 + t].elapsed_time(e[2 + t]) for e in evs for t in range(T)]
     app = [e[1 + T].elapsed_time(e[2 + T]) for e in evs] if wl.appended_per_chunk else []
     att_ms = float(np.mean(att))
-    sel_bytes = [wl.n_q * wl.n_heads * wl.head_dim * 2 + cands[k % n_chunks].numel() * row_means
+    # Q once, the candidates' page means, the top-K_p ids; config 4 also reads
+    # the prompt embeddings and the chunk-to-page map
+    prompt_bytes = (4 * wl.emb_dim * (wl.n_chunk_groups + 1)
+                    + 4 * wl.n_chunk_groups * wl.pages_per_group) if two_stage else 0
+    sel_bytes = [wl.n_q * wl.n_heads * wl.head_dim * 2 + max_cand * row_means + prompt_bytes
+                 + 4 * wl.k_p if two_stage else
+                 wl.n_q * wl.n_heads * wl.head_dim * 2 + cands[k % n_chunks].numel() * row_means
                  + 4 * wl.k_p for k in range(args.steps)]
     sg_bytes = float(np.mean(sel_bytes)) + 2 * 2 * wl.k_p * page_bytes
     sg_ms = float(np.mean(sg))
     value = T * flops_step / (ms_chunk * 1e-3) / 1e12
-    name = "long_horizon" if long_h else "full_history"
-    desc = ("long_horizon: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, 128 "
+    desc = {"long_horizon":
+            "long_horizon: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, 128 "
             "resident pages growing to 136 (one appended per chunk), K_p=4 selected over every "
-            "resident page, 4,680-query chunks, 49,920+4,680 keys, 8 chunks x 4 denoising steps"
-            if long_h else
+            "resident page, 4,680-query chunks, 49,920+4,680 keys, 8 chunks x 4 denoising steps",
+            "full_history":
             "full_history: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, 6 "
             "resident pages all attended (K_p=6), 4,680-query chunk, 74,880+4,680 keys, 4 "
-            "denoising steps with fresh queries and own K/V")
+            "denoising steps with fresh queries and own K/V",
+            "prompt_page":
+            "prompt_page: Wan2.1-1.3B-shaped layer, 12 heads x 128, 12,480-token pages, 64 "
+            "resident pages in 16 past chunks of 4, N(0,1) 4,096-dim prompt embeddings; the "
+            "prompt stage keeps 4 chunks by cosine to the current prompt, the page stage the "
+            "top K_p=4 of their 16 pages; 4,680-query chunk, 49,920+4,680 keys, 1 denoising "
+            "step"}[name]
     result = {
         "metric": "block-attn TFLOP/s (MFMA %) + select/gather HBM GB/s, " + name,
         "value": round(value, 2),
@@ -587,8 +616,8 @@ def bench_chunks(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_chunk, 4),
-        "step": "one chunk: select + gather, %d attention steps%s" % (
-            T, ", append of one page" if wl.appended_per_chunk else ""),
+        "step": "one chunk: select + gather, %d attention step%s%s" % (
+            T, "s" if T > 1 else "", ", append of one page" if wl.appended_per_chunk else ""),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -622,7 +651,8 @@ def bench_chunks(args):
         q_h, ko_h, vo_h = W.chunk_qkv(wl, c_last, T - 1)
         result["cpu_baseline"] = cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means,
                                               args.cpu_seconds, torch,
-                                              n_resident=cands[c_last].numel())
+                                              n_resident=wl.n_pages if two_stage else
+                                              cands[c_last].numel(), prompt_h=prompt_h)
     return result
 
 
@@ -802,7 +832,7 @@ def cpu_model():
 
 
 def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch,
-                 n_resident=None):
+                 n_resident=None, prompt_h=None):
     """The fp64 oracle's attention on a bounded sample of query rows (all heads),
     on the host cores, in the metric's unit (TFLOP/s); the other stages of the
     step (one page mean, the selection, the gather) timed once each beside it."""
@@ -834,7 +864,7 @@ def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch
     n_resident = wl.n_pages if n_resident is None else n_resident
     pm = np.ascontiguousarray(means[:n_resident].cpu().numpy())
     t0 = time.perf_counter()
-    oracle.select_pages(q_h, pm, wl.k_p)
+    oracle.select_pages(q_h, pm, wl.k_p, prompt=prompt_h)
     stages["select"] = time.perf_counter() - t0
     pages = np.ascontiguousarray(k_ctx.reshape(wl.k_p, wl.page_tokens, wl.n_heads, wl.head_dim))
     pages_v = np.ascontiguousarray(v_ctx.reshape(wl.k_p, wl.page_tokens, wl.n_heads, wl.head_dim))
@@ -853,9 +883,10 @@ def cpu_baseline(wl, q_h, k_pool, v_pool, idx, ko_h, vo_h, means, seconds, torch
                   "%.1f s)" % (len(rows), wl.n_q, wl.n_heads, n_k, dt),
         "stages_s": {k: round(v, 4) for k, v in stages.items()},
         "stages_note": "the oracle once each: the mean key of one page, the selection over "
-                       "the %d resident pages (mean query, scores, top-%d), the gather of the "
+                       "the %d resident pages (%smean query, scores, top-%d), the gather of the "
                        "K and V of %d pages (single-threaded; attention uses the cores above)"
-                       % (n_resident, wl.k_p, wl.k_p),
+                       % (n_resident, "prompt stage, " if prompt_h is not None else "", wl.k_p,
+                          wl.k_p),
         "nproc": os.cpu_count(),
         "cpu_model": cpu_model(),
     }
