@@ -7,12 +7,15 @@
 // so the selection is decided in the same precision as the fp64 reference,
 // and repeated calls are bitwise equal.
 //
-// Without a prompt stage and with at most kFusedMaxCand candidates: one
-// launch.  Block (column group, row block) forms the fp64 column sums of its
-// rows of Q and, since alpha is linear in qbar, each candidate's dot product
-// with them over the group's columns; the block that finishes last (a
-// completion counter) adds the block partials of each candidate in block
-// order, scales, ranks and writes the result, then clears the counter.
+// With at most kFusedMaxCand candidates (with a prompt stage: at most
+// kFusedMaxCand pages in all the past chunks): one launch.  Block (column
+// group, row block) forms the fp64 column sums of its rows of Q and, since
+// alpha is linear in qbar, each candidate's dot product with them over the
+// group's columns (with a prompt stage, every chunk's pages; further blocks
+// form the prompt cosines); the block that finishes last (a completion
+// counter) adds the block partials of each candidate in block order, ranks
+// the chunks and keeps their pages (prompt stage), scales, ranks and writes
+// the result, then clears the counter.
 // Otherwise three launches, no host synchronisation:
 //   stage 1  blocks (column group, row block): fp64 partial column sums of Q
 //            (HBM stream); then one block per past chunk: cosine of the
@@ -82,23 +85,34 @@ static constexpr int kFusedBatch = 16;      // rows of a lane in flight together
 // 17.0 us (64) at 48 candidates.
 static constexpr int kFusedGroupChunks = 16;
 
-static bool select_one_launch(int32_t n_cand, int32_t n_chunks) {
-    return n_chunks == 0 && n_cand <= kFusedMaxCand;
+// One launch: at most kFusedMaxCand candidates, or with a prompt stage at
+// most kFusedMaxCand pages in all the past chunks (every chunk's pages are
+// scored, and the last block keeps those of the chunks the prompts select).
+static bool select_one_launch(int32_t n_cand, int32_t n_chunks, int32_t pages_per_chunk) {
+    if (n_chunks == 0) return n_cand <= kFusedMaxCand;
+    return (int64_t)n_chunks * pages_per_chunk <= kFusedMaxCand;
 }
 
 SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
-                          int32_t n_chunks) {
+                          int32_t n_chunks, int32_t pages_per_chunk) {
     SelectWs w;
     // [0, 256): the one-launch path's completion counter, zero between calls;
     // the three-launch path leaves it alone
     size_t off = 256;
-    w.one_launch = select_one_launch(n_cand, n_chunks);
+    w.one_launch = select_one_launch(n_cand, n_chunks, pages_per_chunk);
     if (w.one_launch) {
+        // scored candidates: the list, or with a prompt stage every chunk's pages
+        const int64_t n_all = n_chunks > 0 ? (int64_t)n_chunks * pages_per_chunk : n_cand;
         w.q_plan = colsum_plan(dtype, hd, n_q, kFusedRowsPerLane, kFusedGroupChunks);
         w.groups = w.q_plan.groups;
-        w.alpha_part = off;   // [groups * row blocks][n_cand]
-        off = align_up(off + (size_t)w.q_plan.groups * w.q_plan.blocks * n_cand * sizeof(double), 256);
-        w.partial_q = w.cosine = w.cand = 0;
+        w.alpha_part = off;   // [groups * row blocks][n_all]
+        off = align_up(off + (size_t)w.q_plan.groups * w.q_plan.blocks * n_all * sizeof(double), 256);
+        w.cosine = 0;
+        if (n_chunks > 0) {   // [n_chunks] prompt cosines
+            w.cosine = off;
+            off = align_up(off + (size_t)n_chunks * sizeof(double), 256);
+        }
+        w.partial_q = w.cand = 0;
         w.total = off;
         return w;
     }
@@ -162,6 +176,25 @@ __device__ void block_sum3(double &a, double &b, double &c, double *sh) {
     c = sh[2 * blockDim.x];
 }
 
+// Cosine of the current prompt `cur` with a past chunk's prompt `pm` (fp64,
+// every thread of the block, a fixed order); the result is in thread 0.  A
+// prompt of zero norm has no direction: its cosine is -inf, so that chunk
+// ranks after every other (ties to the lower chunk id), and a zero current
+// prompt leaves the chunks in id order.  `lds` holds 3 * blockDim.x doubles.
+__device__ double prompt_cosine(const float *__restrict__ cur, const float *__restrict__ pm,
+                                int emb_dim, double *lds) {
+    double dot = 0.0, nn = 0.0, pp = 0.0;
+    for (int e = threadIdx.x; e < emb_dim; e += blockDim.x) {
+        const double a = (double)cur[e];
+        const double c = (double)pm[e];
+        dot += a * c;
+        nn += c * c;
+        pp += a * a;
+    }
+    block_sum3(dot, nn, pp, lds);
+    return (pp > 0.0 && nn > 0.0) ? dot / (sqrt(pp) * sqrt(nn)) : -INFINITY;
+}
+
 // Blocks [0, groups * q_blocks): column sums of Q, block b -> (column group
 // b % groups, row block b / groups).  Blocks after those: prompt cosines.
 template <bool BF16>
@@ -182,20 +215,8 @@ __global__ __launch_bounds__(256) void k_select_stage1(
     }
     // prompt stage: cosine of the current prompt with chunk m's prompt
     const int m = b - groups * q_blocks;
-    const float *pm = chunk_prompts + (int64_t)m * emb_dim;
-    double dot = 0.0, nn = 0.0, pp = 0.0;
-    for (int e = threadIdx.x; e < emb_dim; e += blockDim.x) {
-        const double a = (double)cur_prompt[e];
-        const double c = (double)pm[e];
-        dot += a * c;
-        nn += c * c;
-        pp += a * a;
-    }
-    block_sum3(dot, nn, pp, lds);
-    // a prompt of zero norm has no direction: its cosine is -inf, so that
-    // chunk ranks after every other (ties to the lower chunk id), and a zero
-    // current prompt leaves the chunks in id order
-    if (threadIdx.x == 0) cosine[m] = (pp > 0.0 && nn > 0.0) ? dot / (sqrt(pp) * sqrt(nn)) : -INFINITY;
+    const double cs = prompt_cosine(cur_prompt, chunk_prompts + (int64_t)m * emb_dim, emb_dim, lds);
+    if (threadIdx.x == 0) cosine[m] = cs;
 }
 
 // Rank the chunks by (cosine desc, id asc) and write the first n_keep chunk
@@ -409,23 +430,46 @@ __global__ __launch_bounds__(kStage3Threads) void k_select_stage3(
                                                      k_p, recent, n_recent, out_idx, out_scores);
 }
 
-// The one-launch path: kFusedThreads threads per block, block b -> (column
-// group b % groups, row block b / groups), `blocks` = groups * row blocks.
+// The one-launch path: kFusedThreads threads per block, block b < blocks ->
+// (column group b % groups, row block b / groups), `blocks` = groups * row
+// blocks.  With a prompt stage (PROMPT) the candidates scored are every page
+// of every past chunk (cand_in = chunk_pages, n_cand = n_chunks x
+// pages_per_chunk), and blocks blocks ... blocks + n_chunks - 1 each form one
+// chunk's prompt cosine; the last block ranks the chunks, keeps the pages of
+// the first n_keep in rank order, and ranks those.
 static constexpr int kFusedThreads = 256;
-template <bool BF16>
+struct OnePrompt {
+    const float *chunk_prompts;   // [n_chunks][emb_dim]
+    const float *cur_prompt;      // [emb_dim]
+    int emb_dim, n_chunks, pages_per_chunk, n_keep;
+    int32_t *out_chunks;          // [n_keep] or null
+    int32_t *out_cand;            // [n_keep * pages_per_chunk] or null
+    double *cosine;               // workspace [n_chunks]
+};
+template <bool BF16, bool PROMPT>
 __global__ __launch_bounds__(kFusedThreads) void k_select_one(
     const uint4 *__restrict__ q, int64_t n_q, int chunks, int group_chunks, int groups,
-    int row_lanes, int rows_per_block, int blocks, const double *__restrict__ page_means,
-    int64_t hd, int max_pages, const int32_t *__restrict__ cand_in, int n_cand, double denom, int k_p,
+    int row_lanes, int rows_per_block, int blocks, int grid_blocks,
+    const double *__restrict__ page_means, int64_t hd, int max_pages,
+    const int32_t *__restrict__ cand_in, int n_cand, double denom, int k_p,
     const int32_t *__restrict__ recent, int n_recent, int *__restrict__ counter,
     double *__restrict__ alpha_blk, int32_t *__restrict__ out_idx,
-    double *__restrict__ out_scores) {
+    double *__restrict__ out_scores, OnePrompt pr) {
     constexpr int VEC = BF16 ? 8 : 4;
     __shared__ double lds[kFusedThreads * VEC];   // row-lane partials of colsum_block
     __shared__ double colsum[64 * VEC];           // this block's column sums
     __shared__ double alpha[kFusedThreads];
     __shared__ int last;
     const int t = threadIdx.x, b = blockIdx.x;
+    int ncp = 4;
+    while (ncp < n_cand) ncp <<= 1;
+    if (PROMPT && b >= blocks) {
+        // prompt cosine of chunk b - blocks
+        const int m = b - blocks;
+        const double cs = prompt_cosine(pr.cur_prompt, pr.chunk_prompts + (int64_t)m * pr.emb_dim,
+                                        pr.emb_dim, lds);
+        if (t == 0) __hip_atomic_store(pr.cosine + m, cs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
     const int g = b % groups, rb = b / groups;
     const int c0 = g * group_chunks;
     const int gw = min(group_chunks, chunks - c0) * VEC;   // columns in this group
@@ -437,8 +481,6 @@ __global__ __launch_bounds__(kFusedThreads) void k_select_one(
     // consecutive lanes per candidate (ncp = n_cand rounded up to a power of
     // two, at least 4); lane sub adds columns sub, sub + tpc, ... in order,
     // 8 loads in flight at a time, then a butterfly over the tpc lanes
-    int ncp = 4;
-    while (ncp < n_cand) ncp <<= 1;
     const int tpc = kFusedThreads / ncp;
     {
         const int j = t / tpc, sub = t % tpc;
@@ -461,13 +503,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_select_one(
             __hip_atomic_store(alpha_blk + (int64_t)b * n_cand + j, v, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
+    }
     // this wavefront's stores have reached the coherent level; once every
     // wavefront is past the barrier, the block counts itself done
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t == 0)
         last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               blocks - 1;
+               grid_blocks - 1;
     __syncthreads();
     if (!last) return;
 
@@ -496,14 +539,36 @@ __global__ __launch_bounds__(kFusedThreads) void k_select_one(
         alpha[t] = v;   // alpha[sl * ncp + j]
     }
     __syncthreads();
-    auto alpha_of = [&](int j) -> double {
+    auto slice_sum = [&](int j) -> double {
         double v = 0.0;
         for (int sl = 0; sl < slices; ++sl) v += alpha[sl * ncp + j];
         return v;
     };
-    auto id_of = [&](int j) -> int { return cand_in ? cand_in[j] : j; };
-    finish_select<kFusedThreads, kFusedMaxCand>(alpha_of, id_of, n_cand, max_pages, denom, k_p,
-                                                recent, n_recent, out_idx, out_scores);
+    if constexpr (PROMPT) {
+        // the chunks in (cosine desc, id asc) order, the first n_keep kept;
+        // candidate j is page j % ppc of the (j / ppc)-th kept chunk
+        __shared__ double cosl[kFusedMaxCand];
+        __shared__ int kept[kFusedMaxCand];
+        for (int m = t; m < pr.n_chunks; m += kFusedThreads)
+            cosl[m] = __hip_atomic_load(pr.cosine + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (t < 64) rank_chunks(cosl, pr.n_chunks, pr.n_keep, kept);
+        __syncthreads();
+        const int ppc = pr.pages_per_chunk, n_kept = pr.n_keep * ppc;
+        auto src = [&](int j) -> int { return kept[j / ppc] * ppc + j % ppc; };
+        if (pr.out_chunks)
+            for (int r = t; r < pr.n_keep; r += kFusedThreads) pr.out_chunks[r] = kept[r];
+        if (pr.out_cand)
+            for (int j = t; j < n_kept; j += kFusedThreads) pr.out_cand[j] = cand_in[src(j)];
+        auto alpha_of = [&](int j) -> double { return slice_sum(src(j)); };
+        auto id_of = [&](int j) -> int { return cand_in[src(j)]; };
+        finish_select<kFusedThreads, kFusedMaxCand>(alpha_of, id_of, n_kept, max_pages, denom,
+                                                    k_p, recent, n_recent, out_idx, out_scores);
+    } else {
+        auto id_of = [&](int j) -> int { return cand_in ? cand_in[j] : j; };
+        finish_select<kFusedThreads, kFusedMaxCand>(slice_sum, id_of, n_cand, max_pages, denom,
+                                                    k_p, recent, n_recent, out_idx, out_scores);
+    }
     // ready for the next call on this workspace
     if (t == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -514,21 +579,38 @@ hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const d
                          double *out_scores, void *ws, hipStream_t s) {
     const int64_t hd = (int64_t)L.n_heads * L.head_dim;
     const int n_chunks = prompt ? prompt->n_chunks : 0;
-    const SelectWs w = select_workspace(L.dtype, hd, n_q, n_cand, n_chunks);
+    const SelectWs w = select_workspace(L.dtype, hd, n_q, n_cand, n_chunks,
+                                        prompt ? prompt->pages_per_chunk : 0);
     char *base = (char *)ws;
     if (w.one_launch) {
         const ColSumPlan &p = w.q_plan;
         const double denom = (double)n_q * sqrt((double)L.head_dim);
+        OnePrompt pr{};
+        int n_scored = n_cand;
+        const int32_t *scored = cand;
+        if (prompt) {
+            pr = OnePrompt{prompt->chunk_prompts, prompt->cur_prompt, prompt->emb_dim, n_chunks,
+                           prompt->pages_per_chunk, prompt->n_keep, prompt->out_chunks,
+                           prompt->out_cand, (double *)(base + w.cosine)};
+            n_scored = n_chunks * prompt->pages_per_chunk;
+            scored = prompt->chunk_pages;
+        }
+        const int blocks = p.groups * p.blocks;
+        const int grid = blocks + n_chunks;
         auto launch = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3(p.groups * p.blocks), dim3(kFusedThreads), 0, s,
-                               (const uint4 *)q, (int64_t)n_q, p.chunks, p.group_chunks, p.groups,
-                               p.row_lanes, p.rows_per_block, p.groups * p.blocks, page_means, hd,
-                               L.max_pages, cand,
-                               n_cand, denom, k_p, recent, n_recent, (int *)base,
-                               (double *)(base + w.alpha_part), out_idx, out_scores);
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(kFusedThreads), 0, s, (const uint4 *)q,
+                               (int64_t)n_q, p.chunks, p.group_chunks, p.groups, p.row_lanes,
+                               p.rows_per_block, blocks, grid, page_means, hd, L.max_pages, scored,
+                               n_scored, denom, k_p, recent, n_recent, (int *)base,
+                               (double *)(base + w.alpha_part), out_idx, out_scores, pr);
         };
-        if (L.dtype == WA_BF16) launch(k_select_one<true>);
-        else launch(k_select_one<false>);
+        if (L.dtype == WA_BF16) {
+            if (prompt) launch(k_select_one<true, true>);
+            else launch(k_select_one<true, false>);
+        } else {
+            if (prompt) launch(k_select_one<false, true>);
+            else launch(k_select_one<false, false>);
+        }
         return hipGetLastError();
     }
     double *partial_q = (double *)(base + w.partial_q);

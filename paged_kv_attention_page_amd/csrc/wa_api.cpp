@@ -73,7 +73,12 @@ size_t wa_select_workspace_bytes(const wa_layout *L, int32_t n_q, int32_t n_cand
     if (n_cand > WA_MAX_CANDIDATES) return 0;
     const int32_t n_chunks = prompt ? prompt->n_chunks : 0;
     if (n_chunks < 0 || n_chunks > WA_MAX_CANDIDATES) return 0;
-    return select_workspace(L->dtype, (int64_t)L->n_heads * L->head_dim, n_q, n_cand, n_chunks)
+    if (prompt && (n_chunks < 1 || prompt->pages_per_chunk < 1 || prompt->n_keep < 1 ||
+                   prompt->n_keep > n_chunks ||
+                   (int64_t)prompt->n_keep * prompt->pages_per_chunk != n_cand))
+        return 0;
+    return select_workspace(L->dtype, (int64_t)L->n_heads * L->head_dim, n_q, n_cand, n_chunks,
+                            prompt ? prompt->pages_per_chunk : 0)
         .total;
 }
 

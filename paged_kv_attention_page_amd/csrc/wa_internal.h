@@ -47,9 +47,9 @@ size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens);
 // Bytes [0, 256) hold the one-launch path's completion counter (zero between
 // calls).  One-launch path: alpha_part is [groups * row blocks][n_cand].
 struct SelectWs {
-    bool one_launch;    // no prompt stage, few candidates: one kernel
+    bool one_launch;    // few candidates (with a prompt stage: few pages in all the chunks): one kernel
     size_t partial_q;   // [q_blocks][hd] double
-    size_t cosine;      // [n_chunks] double
+    size_t cosine;      // [n_chunks] double (prompt stage)
     size_t alpha_part;  // [groups][n_cand] double
     size_t cand;        // [n_cand] int32
     size_t total;
@@ -57,7 +57,7 @@ struct SelectWs {
     int groups;
 };
 SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
-                          int32_t n_chunks);
+                          int32_t n_chunks, int32_t pages_per_chunk);
 // Device address of this device's fixed selection workspace (the `scratch`
 // array of k_select.hip, WA_SELECT_NOALLOC_MAX_WORKSPACE bytes), looked up
 // once per device; allocates nothing.

@@ -303,6 +303,41 @@ def test_selection_follows_pool_slots_under_permutation():
     assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
 
 
+@pytest.mark.parametrize("n_chunks", [16, 20])
+def test_prompt_stage_with_window(n_chunks):
+    """wa_select_window with a prompt stage: the window's ids first, then the
+    top K_p of the kept chunks' pages outside the window, against the oracle;
+    the window holds one page of the best-ranked chunk and one page no kept
+    chunk holds.  16 chunks of 4 pages take the one-launch selection, 20 the
+    three-launch one."""
+    wl = W.scaled(W.WORKLOADS["prompt_page"], name="prompt_window_%d" % n_chunks, n_heads=2,
+                  frame_tokens=10, n_chunk_groups=n_chunks, n_pages=4 * n_chunks)
+    run = PoolRun(wl)
+    for j in range(wl.n_pages):
+        run.append(j)
+    cp, cur, pages = W.chunk_prompts(wl), W.current_prompt(wl), W.chunk_page_map(wl)
+    host_prompt = dict(chunk_prompts=cp, cur_prompt=cur, chunk_pages=pages,
+                       n_keep=wl.n_cand_groups)
+    q, _, _ = W.chunk_qkv(wl, 0, 0)
+    host_means = run.oracle_means(range(wl.n_pages))
+    plain = oracle.select_pages(q, host_means, wl.k_p, prompt=host_prompt)
+    best = int(plain["chunks"][0])
+    outside = [m for m in range(n_chunks) if m not in plain["chunks"].tolist()][0]
+    recent = np.array([pages[best][1], pages[outside][0]], dtype=np.int32)
+    dev_prompt = dict(chunk_prompts=torch.from_numpy(cp).cuda(),
+                      cur_prompt=torch.from_numpy(cur).cuda(),
+                      chunk_pages=torch.from_numpy(pages).cuda(), n_keep=wl.n_cand_groups)
+    say("prompt stage with a window:", n_chunks, "chunks, recent", recent.tolist())
+    scores = torch.empty(wl.n_cand_groups * wl.pages_per_group, dtype=torch.float64,
+                         device="cuda")
+    idx = wa.wa_select_window(run.L, to_device(q), run.means, torch.from_numpy(recent).cuda(),
+                              wl.k_p, prompt=dev_prompt, out_scores=scores)
+    ref = oracle.select_window(q, host_means, wl.k_p, recent, prompt=host_prompt)
+    assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+    got = scores.cpu().numpy()
+    assert np.abs(got - ref["alpha"]).max() <= 1e-12 * max(1.0, np.abs(ref["alpha"]).max())
+
+
 @pytest.mark.parametrize("zero", ["chunk_prompts", "cur_prompt"])
 def test_prompt_stage_with_zero_norm_prompts(zero):
     """A prompt embedding of zero norm has no direction: its cosine is -inf on

@@ -152,10 +152,14 @@ def test_wan_kp4_full_size_sampled_rows():
     check_attention(wl, q, hk, hv, ko, vo, k_ctx, v_ctx, rows=rows)
 
 
-def test_prompt_stage_pipeline():
-    """Prompt stage over 16 chunks of 4 pages (4,096-dim prompts), then the page
-    stage over the 4 kept chunks' 16 pages; small pages keep the oracle fast."""
-    wl = W.scaled(W.WORKLOADS["prompt_page"], name="prompt_small", n_heads=2, frame_tokens=10)
+@pytest.mark.parametrize("n_chunks", [16, 20])
+def test_prompt_stage_pipeline(n_chunks):
+    """Prompt stage over 16 (or 20) chunks of 4 pages (4,096-dim prompts), then
+    the page stage over the 4 kept chunks' 16 pages; small pages keep the
+    oracle fast.  64 pages in all take the one-launch selection, 80 the
+    three-launch one."""
+    wl = W.scaled(W.WORKLOADS["prompt_page"], name="prompt_small_%d" % n_chunks, n_heads=2,
+                  frame_tokens=10, n_chunk_groups=n_chunks, n_pages=4 * n_chunks)
     run = PoolRun(wl)
     for j in range(wl.n_pages):
         run.append(j)
