@@ -470,39 +470,39 @@ __global__ __launch_bounds__(kFusedThreads) void k_select_one(
                                         pr.emb_dim, lds);
         if (t == 0) __hip_atomic_store(pr.cosine + m, cs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-    const int g = b % groups, rb = b / groups;
-    const int c0 = g * group_chunks;
-    const int gw = min(group_chunks, chunks - c0) * VEC;   // columns in this group
-    colsum_block<BF16, kFusedBatch>(q, nullptr, nullptr, nullptr, n_q, chunks, c0, group_chunks,
-                                    row_lanes, rows_per_block, rb, lds, colsum, c0 * VEC);
-    __syncthreads();
+        const int g = b % groups, rb = b / groups;
+        const int c0 = g * group_chunks;
+        const int gw = min(group_chunks, chunks - c0) * VEC;   // columns in this group
+        colsum_block<BF16, kFusedBatch>(q, nullptr, nullptr, nullptr, n_q, chunks, c0, group_chunks,
+                                        row_lanes, rows_per_block, rb, lds, colsum, c0 * VEC);
+        __syncthreads();
 
-    // candidate j's dot product with this block's column sums: tpc = 256 / ncp
-    // consecutive lanes per candidate (ncp = n_cand rounded up to a power of
-    // two, at least 4); lane sub adds columns sub, sub + tpc, ... in order,
-    // 8 loads in flight at a time, then a butterfly over the tpc lanes
-    const int tpc = kFusedThreads / ncp;
-    {
-        const int j = t / tpc, sub = t % tpc;
-        const int id = j < n_cand ? (cand_in ? cand_in[j] : j) : -1;
-        double v = 0.0;
-        if (id >= 0 && id < max_pages) {
-            const double *pm = page_means + (int64_t)id * hd + (int64_t)c0 * VEC;
-            int c = sub;
-            for (; c + 7 * tpc < gw; c += 8 * tpc) {
-                double x[8];
+        // candidate j's dot product with this block's column sums: tpc = 256 / ncp
+        // consecutive lanes per candidate (ncp = n_cand rounded up to a power of
+        // two, at least 4); lane sub adds columns sub, sub + tpc, ... in order,
+        // 8 loads in flight at a time, then a butterfly over the tpc lanes
+        const int tpc = kFusedThreads / ncp;
+        {
+            const int j = t / tpc, sub = t % tpc;
+            const int id = j < n_cand ? (cand_in ? cand_in[j] : j) : -1;
+            double v = 0.0;
+            if (id >= 0 && id < max_pages) {
+                const double *pm = page_means + (int64_t)id * hd + (int64_t)c0 * VEC;
+                int c = sub;
+                for (; c + 7 * tpc < gw; c += 8 * tpc) {
+                    double x[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) x[u] = pm[c + u * tpc];
+                    for (int u = 0; u < 8; ++u) x[u] = pm[c + u * tpc];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v += colsum[c + u * tpc] * x[u];
+                    for (int u = 0; u < 8; ++u) v += colsum[c + u * tpc] * x[u];
+                }
+                for (; c < gw; c += tpc) v += colsum[c] * pm[c];
             }
-            for (; c < gw; c += tpc) v += colsum[c] * pm[c];
+            for (int off = tpc >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            if (sub == 0 && j < n_cand)
+                __hip_atomic_store(alpha_blk + (int64_t)b * n_cand + j, v, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        for (int off = tpc >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        if (sub == 0 && j < n_cand)
-            __hip_atomic_store(alpha_blk + (int64_t)b * n_cand + j, v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
     }
     // this wavefront's stores have reached the coherent level; once every
     // wavefront is past the barrier, the block counts itself done
