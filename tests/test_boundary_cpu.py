@@ -208,6 +208,22 @@ def _prompt(n_chunks=16, emb=4096, ppc=4, keep=4):
     return wa.PromptStage(0x30000, 0x40000, 0x50000, n_chunks, emb, ppc, keep, None, None)
 
 
+def test_select_workspace_size_with_prompt_stage(lib):
+    """With a prompt stage the workspace depends on the prompt's shape: an
+    inconsistent one gets 0 (as the selection itself rejects it), and the
+    one-launch layout holds a partial score for every page of every chunk, so
+    fewer chunks need less room."""
+    ws = lambda n_cand, p: lib.wa_select_workspace_bytes(L(), 4680, n_cand, ctypes.byref(p))
+    full = ws(16, _prompt())                          # 16 chunks x 4 pages: one launch
+    assert full > 0
+    assert ws(16, _prompt(n_chunks=8)) < full         # 32 pages scored instead of 64
+    assert ws(12, _prompt()) == 0                     # n_cand != n_keep * pages_per_chunk
+    assert ws(16, _prompt(keep=17)) == 0              # n_keep > n_chunks
+    assert ws(16, _prompt(ppc=0, keep=4)) == 0
+    assert ws(16, _prompt(keep=0)) == 0
+    assert ws(16, _prompt(n_chunks=17)) > 0           # 68 pages: three launches
+
+
 def test_select_rejects_bad_prompt_stage(lib):
     E, U = wa.WA_ERR_INVALID_ARG, wa.WA_ERR_UNSUPPORTED
     ok = _prompt()
