@@ -158,7 +158,7 @@ wa_status wa_append_page(const wa_layout *layout, const void *k_src, const void 
 /*
  * Bytes of device workspace wa_select_pages needs (0 if the arguments are
  * invalid).  prompt may be NULL.  The workspace must be zero-filled before
- * its first use (it holds a completion counter); every call leaves it
+ * its first use (its first 256 bytes hold completion counters); every call leaves it
  * zero-filled where that matters again, so one workspace serves any number
  * of calls ordered on one stream.  Calls that overlap on one workspace race.
  */

@@ -16,6 +16,11 @@
 // counter) adds the block partials of each candidate in block order, ranks
 // the chunks and keeps their pages (prompt stage), scales, ranks and writes
 // the result, then clears the counter.
+// With 65 to 256 candidates and no prompt stage: one launch in two levels.
+// Block (column group, row block) publishes its column sums; the last row
+// block of each column group adds them and forms every candidate's partial
+// dot product over the group's columns; the last group adds those, ranks
+// (K_p rounds of a wavefront argmax) and clears the counters.
 // Otherwise three launches, no host synchronisation:
 //   stage 1  blocks (column group, row block): fp64 partial column sums of Q
 //            (HBM stream); then one block per past chunk: cosine of the
@@ -84,10 +89,23 @@ static constexpr int kFusedBatch = 16;      // rows of a lane in flight together
 // 16, 32 or 64 vectors at 16 candidates, but 14.4 us against 16.0 (32) and
 // 17.0 us (64) at 48 candidates.
 static constexpr int kFusedGroupChunks = 16;
+// Candidates of the two-level one-launch path (more than kFusedMaxCand, no
+// prompt stage); its ranking takes K_p rounds of a wavefront argmax beyond
+// 64 candidates (a per-candidate count would compare every pair).
+static constexpr int kWideMaxCand = 256;
+static constexpr int kWideGroupChunks = 8;   // column group: 8 vectors (64 bf16 columns)
+static constexpr int kWideRounds = 8;        // candidate rounds of partial dots in flight
+// (At 136 candidates on a 4,680 x 1,536 bf16 chunk: 16.9 us against 22.4 us
+// for the three launches; groups of 16 or 4 vectors measured slower, 2 or 4
+// rounds in flight no faster.)
 
 // One launch: at most kFusedMaxCand candidates, or with a prompt stage at
 // most kFusedMaxCand pages in all the past chunks (every chunk's pages are
 // scored, and the last block keeps those of the chunks the prompts select).
+static bool select_wide(int32_t n_cand, int32_t n_chunks) {
+    return n_chunks == 0 && n_cand > kFusedMaxCand && n_cand <= kWideMaxCand;
+}
+
 static bool select_one_launch(int32_t n_cand, int32_t n_chunks, int32_t pages_per_chunk) {
     if (n_chunks == 0) return n_cand <= kFusedMaxCand;
     return (int64_t)n_chunks * pages_per_chunk <= kFusedMaxCand;
@@ -100,6 +118,21 @@ SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand
     // the three-launch path leaves it alone
     size_t off = 256;
     w.one_launch = select_one_launch(n_cand, n_chunks, pages_per_chunk);
+    w.wide = false;
+    if (!w.one_launch && select_wide(n_cand, n_chunks) &&
+        colsum_plan(dtype, hd, n_q, kFusedRowsPerLane, kWideGroupChunks).groups < 64) {
+        // [0, 256) holds the final counter, then one counter per column group
+        w.wide = true;
+        w.q_plan = colsum_plan(dtype, hd, n_q, kFusedRowsPerLane, kWideGroupChunks);
+        w.groups = w.q_plan.groups;
+        w.partial_q = off;    // [row blocks][hd] column sums
+        off = align_up(off + (size_t)w.q_plan.blocks * hd * sizeof(double), 256);
+        w.alpha_part = off;   // [groups][n_cand]
+        off = align_up(off + (size_t)w.groups * n_cand * sizeof(double), 256);
+        w.cosine = w.cand = 0;
+        w.total = off;
+        return w;
+    }
     if (w.one_launch) {
         // scored candidates: the list, or with a prompt stage every chunk's pages
         const int64_t n_all = n_chunks > 0 ? (int64_t)n_chunks * pages_per_chunk : n_cand;
@@ -140,7 +173,69 @@ __device__ __forceinline__ bool ranks_before(double sa, int ia, int ja, double s
 
 // Butterfly argmax over the 64 lanes of a wavefront; every lane ends with the
 // same winner because the order is total.
+// x from another lane of the wavefront by a DPP lane permutation (CTRL; every
+// lane's source exists), both 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const long long u = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xf, 0xf, false);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Maximum over the 64 lanes, in every lane: within quads (DPP quad_perm
+// [1,0,3,2], [2,3,0,1]), half-rows (row_half_mirror) and rows (row_mirror),
+// then across rows and halves (permlane16 / permlane32 swaps).  All lanes
+// must be active.
+__device__ __forceinline__ double wave_max_f64(double m) {
+    m = fmax(m, dpp_f64<0xb1>(m));
+    m = fmax(m, dpp_f64<0x4e>(m));
+    m = fmax(m, dpp_f64<0x141>(m));
+    m = fmax(m, dpp_f64<0x140>(m));
+    {
+        const long long u = __double_as_longlong(m);
+        const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(u >> 32),
+                                                         false, false);
+        m = fmax(__longlong_as_double(((long long)hi[0] << 32) | lo[0]),
+                 __longlong_as_double(((long long)hi[1] << 32) | lo[1]));
+    }
+    {
+        const long long u = __double_as_longlong(m);
+        const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32),
+                                                         false, false);
+        m = fmax(__longlong_as_double(((long long)hi[0] << 32) | lo[0]),
+                 __longlong_as_double(((long long)hi[1] << 32) | lo[1]));
+    }
+    return m;
+}
+
+// The highest score among the lanes holding an item comes from a maximum over
+// the score alone; a ballot then finds the lanes holding it, and only when
+// several do (a tie) does a butterfly over the whole order run among them.
+// All 64 lanes must be active.
 __device__ __forceinline__ void wave_argmax(double &s, int &id, int &pos) {
+    const double m = wave_max_f64(id >= 0 ? s : -INFINITY);
+    const unsigned long long tied = __builtin_amdgcn_ballot_w64(id >= 0 && s == m);
+    if (tied == 0ull) {   // no lane holds an item
+        s = 0.0;
+        id = -1;
+        pos = -1;
+        return;
+    }
+    if ((tied & (tied - 1ull)) == 0ull) {   // one lane holds the highest score
+        const int l = __builtin_ctzll(tied);
+        s = m;
+        id = __builtin_amdgcn_readlane(id, l);
+        pos = __builtin_amdgcn_readlane(pos, l);
+        return;
+    }
+    if (!((tied >> (threadIdx.x & 63)) & 1ull)) {
+        s = 0.0;
+        id = -1;
+        pos = -1;
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const double os = __shfl_xor(s, off, 64);
@@ -315,7 +410,7 @@ __global__ __launch_bounds__(kStage2Threads) void k_select_stage2(const double *
 // NT: the block's thread count.  (The block size is a template argument, not
 // blockDim: reading it, or __syncthreads_count, fetches the launch's size
 // from memory on the critical path.)
-template <int NT, int MAXC, class AlphaOf, class IdOf>
+template <int NT, int MAXC, int RANK_MAX = NT, class AlphaOf, class IdOf>
 __device__ void finish_select(AlphaOf alpha_of, IdOf id_of, int n_cand, int max_pages,
                               double denom, int k_p, const int32_t *__restrict__ recent,
                               int n_recent, int32_t *__restrict__ out_idx,
@@ -345,7 +440,7 @@ __device__ void finish_select(AlphaOf alpha_of, IdOf id_of, int n_cand, int max_
     }
     __syncthreads();
 
-    if (n_cand <= NT) {
+    if (n_cand <= RANK_MAX) {
         // rank of candidate j = number of candidates ordered before it, found
         // by lpc consecutive lanes (lpc = NT / ncp, at most a wavefront; ncp =
         // n_cand rounded up to a power of two): lane sub compares candidates
@@ -381,6 +476,36 @@ __device__ void finish_select(AlphaOf alpha_of, IdOf id_of, int n_cand, int max_
     // j lives in lane j % 64, slot j / 64
     if (t >= 64) return;
     const int lane = t;
+    if constexpr (MAXC <= 4 * 64) {
+        // at most 4 candidates per lane: held in registers for every round
+        constexpr int PL = (MAXC + 63) / 64;
+        double sv[PL];
+        int iv[PL];
+#pragma unroll
+        for (int u = 0; u < PL; ++u) {
+            const int j = lane + 64 * u;
+            sv[u] = j < n_cand ? sc[j] : 0.0;
+            iv[u] = j < n_cand ? ids[j] : -1;   // -1: no item, never ranked
+        }
+        unsigned taken = 0u;
+        for (int r = 0; r < k_p; ++r) {
+            double bs = 0.0;
+            int bid = -1, bpos = -1;
+#pragma unroll
+            for (int u = 0; u < PL; ++u) {
+                const int j = lane + 64 * u;
+                if (!((taken >> u) & 1u) && ranks_before(sv[u], iv[u], j, bs, bid, bpos)) {
+                    bs = sv[u];
+                    bid = iv[u];
+                    bpos = j;
+                }
+            }
+            wave_argmax(bs, bid, bpos);
+            if (bpos >= 0 && (bpos & 63) == lane) taken |= 1u << (bpos >> 6);
+            if (lane == 0) out_idx[r] = bid;     // -1 when nothing valid is left
+        }
+        return;
+    }
     const int per_lane = (n_cand + 63) / 64;   // <= 64
     unsigned long long taken = 0ull;
     for (int u = 0; u < per_lane; ++u) {
@@ -573,6 +698,155 @@ __global__ __launch_bounds__(kFusedThreads) void k_select_one(
     if (t == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The two-level one-launch path (kFusedMaxCand < n_cand <= kWideMaxCand, no
+// prompt stage).  Block (column group g, row block rb) forms the fp64 column
+// sums of its rows of Q over the group's columns and publishes them
+// (agent-scope stores); the last row block of group g to finish (its own
+// counter) adds the group's row-block sums in row-block order and forms each
+// candidate's partial dot product over the group's columns; the last group to
+// finish (the final counter) adds the group partials in group order, scales,
+// ranks and writes the result, then clears every counter.
+template <bool BF16>
+__global__ __launch_bounds__(kFusedThreads) void k_select_wide(
+    const uint4 *__restrict__ q, int64_t n_q, int chunks, int group_chunks, int groups,
+    int row_lanes, int rows_per_block, int row_blocks, const double *__restrict__ page_means,
+    int64_t hd, int max_pages, const int32_t *__restrict__ cand_in, int n_cand, double denom,
+    int k_p, const int32_t *__restrict__ recent, int n_recent, int *__restrict__ counters,
+    double *__restrict__ colpart, double *__restrict__ gpart, int32_t *__restrict__ out_idx,
+    double *__restrict__ out_scores) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    constexpr int NT = kFusedThreads;
+    __shared__ double lds[NT * VEC];    // row-lane partials of colsum_block, then a scratch
+    __shared__ double colsum[64 * VEC];
+    __shared__ double alpha[kWideMaxCand];
+    __shared__ int cid[kWideMaxCand];
+    __shared__ int flag;
+    const int t = threadIdx.x, b = blockIdx.x;
+    const int g = b % groups, rb = b / groups;
+    const int c0 = g * group_chunks;
+    const int gw = min(group_chunks, chunks - c0) * VEC;   // columns in this group
+    colsum_block<BF16, kFusedBatch>(q, nullptr, nullptr, nullptr, n_q, chunks, c0, group_chunks,
+                                    row_lanes, rows_per_block, rb, lds, colsum, c0 * VEC);
+    __syncthreads();
+    double *const my_cols = colpart + (int64_t)rb * hd + (int64_t)c0 * VEC;
+    for (int c = t; c < gw; c += NT)
+        __hip_atomic_store(my_cols + c, colsum[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0)
+        flag = __hip_atomic_fetch_add(counters + 1 + g, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == row_blocks - 1;
+    __syncthreads();
+    if (!flag) return;
+
+    // last row block of group g: column c's sum over the row blocks, split
+    // over `splits` lanes (lane s adds row blocks s, s + splits, ... in order,
+    // then the splits are added in order)
+    const int splits = NT / gw;   // >= 1 (gw <= kWideGroupChunks vectors)
+    // the candidate ids, read while the column sums are on their way
+    for (int j = t; j < n_cand; j += NT) cid[j] = cand_in ? cand_in[j] : j;
+    {
+        const int c = t % gw, sp = t / gw;
+        double v = 0.0;
+        if (sp < splits) {
+            const double *col = colpart + (int64_t)c0 * VEC + c;
+            const int terms = sp < row_blocks ? (row_blocks - 1 - sp) / splits + 1 : 0;
+            for (int u0 = 0; u0 < terms; u0 += 16) {
+                double x[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    x[u] = u0 + u < terms
+                               ? __hip_atomic_load(col + (int64_t)(sp + (u0 + u) * splits) * hd,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.0;
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (u0 + u < terms) v += x[u];
+            }
+            lds[sp * gw + c] = v;
+        }
+    }
+    __syncthreads();
+    if (t < gw) {
+        double v = 0.0;
+        for (int sp = 0; sp < splits; ++sp) v += lds[sp * gw + t];
+        colsum[t] = v;   // the group's column sums over all of Q
+    }
+    __syncthreads();
+
+    // partial dot products over the group's columns: 8 lanes per candidate,
+    // 32 candidates per round, kWideRounds rounds' loads in flight together;
+    // lane sub adds columns sub, sub + 8, ... in order, then a butterfly over
+    // the 8 lanes
+    {
+        constexpr int U = kWideGroupChunks * VEC / 8;   // columns of a lane per candidate
+        const int sub = t & 7, slot = t >> 3;
+        for (int j0 = 0; j0 < n_cand; j0 += (NT / 8) * kWideRounds) {
+            double x[kWideRounds][U];
+#pragma unroll
+            for (int r = 0; r < kWideRounds; ++r) {
+                const int j = j0 + (NT / 8) * r + slot;
+                const int id = j < n_cand ? cid[j] : -1;
+                const bool ok = id >= 0 && id < max_pages;
+                const double *pm = page_means + (int64_t)(ok ? id : 0) * hd + (int64_t)c0 * VEC;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = sub + 8 * u;
+                    x[r][u] = ok && c < gw ? pm[c] : 0.0;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kWideRounds; ++r) {
+                double v = 0.0;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = sub + 8 * u;
+                    if (c < gw) v += colsum[c] * x[r][u];
+                }
+                v += __shfl_xor(v, 4, 64);
+                v += __shfl_xor(v, 2, 64);
+                v += __shfl_xor(v, 1, 64);
+                const int j = j0 + (NT / 8) * r + slot;
+                if (sub == 0 && j < n_cand)
+                    __hip_atomic_store(gpart + (int64_t)g * n_cand + j, v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0)
+        flag = __hip_atomic_fetch_add(counters, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               groups - 1;
+    __syncthreads();
+    if (!flag) return;
+
+    // the last group: alpha_j = the group partials of candidate j in group order
+    for (int j = t; j < n_cand; j += NT) {
+        double v = 0.0;
+        for (int g0 = 0; g0 < groups; g0 += 32) {
+            double x[32];   // up to 32 loads in flight, then added in group order
+#pragma unroll
+            for (int u = 0; u < 32; ++u)
+                x[u] = g0 + u < groups
+                           ? __hip_atomic_load(gpart + (int64_t)(g0 + u) * n_cand + j,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.0;
+#pragma unroll
+            for (int u = 0; u < 32; ++u)
+                if (g0 + u < groups) v += x[u];
+        }
+        alpha[j] = v;
+    }
+    __syncthreads();
+    auto alpha_of = [&](int j) -> double { return alpha[j]; };
+    auto id_of = [&](int j) -> int { return cid[j]; };
+    finish_select<NT, kWideMaxCand, kFusedMaxCand>(alpha_of, id_of, n_cand, max_pages, denom, k_p,
+                                                   recent, n_recent, out_idx, out_scores);
+    // ready for the next call on this workspace
+    if (t <= groups) __hip_atomic_store(counters + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const double *page_means,
                          const int32_t *cand, int32_t n_cand, const wa_prompt_stage *prompt,
                          const int32_t *recent, int32_t n_recent, int32_t k_p, int32_t *out_idx,
@@ -611,6 +885,21 @@ hipError_t launch_select(const wa_layout &L, const void *q, int32_t n_q, const d
             if (prompt) launch(k_select_one<false, true>);
             else launch(k_select_one<false, false>);
         }
+        return hipGetLastError();
+    }
+    if (w.wide) {
+        const ColSumPlan &p = w.q_plan;
+        const double denom = (double)n_q * sqrt((double)L.head_dim);
+        auto launch = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(p.groups * p.blocks), dim3(kFusedThreads), 0, s,
+                               (const uint4 *)q, (int64_t)n_q, p.chunks, p.group_chunks, p.groups,
+                               p.row_lanes, p.rows_per_block, p.blocks, page_means, hd,
+                               L.max_pages, cand, n_cand, denom, k_p, recent, n_recent,
+                               (int *)base, (double *)(base + w.partial_q),
+                               (double *)(base + w.alpha_part), out_idx, out_scores);
+        };
+        if (L.dtype == WA_BF16) launch(k_select_wide<true>);
+        else launch(k_select_wide<false>);
         return hipGetLastError();
     }
     double *partial_q = (double *)(base + w.partial_q);

@@ -44,10 +44,12 @@ ColSumPlan colsum_plan(int32_t dtype, int64_t hd, int64_t rows, int rows_per_lan
 
 size_t append_workspace_bytes(int32_t dtype, int64_t hd, int64_t page_tokens);
 
-// Bytes [0, 256) hold the one-launch path's completion counter (zero between
-// calls).  One-launch path: alpha_part is [groups * row blocks][n_cand].
+// Bytes [0, 256) hold the one-launch paths' completion counters (zero between
+// calls).  One-launch path: alpha_part is [groups * row blocks][n_cand]; two-level
+// path: partial_q is [row blocks][hd] column sums, alpha_part [groups][n_cand].
 struct SelectWs {
     bool one_launch;    // few candidates (with a prompt stage: few pages in all the chunks): one kernel
+    bool wide;          // up to 256 candidates, no prompt stage: one kernel, two-level hand-off
     size_t partial_q;   // [q_blocks][hd] double
     size_t cosine;      // [n_chunks] double (prompt stage)
     size_t alpha_part;  // [groups][n_cand] double

@@ -384,9 +384,11 @@ def test_prompt_stage_with_zero_norm_prompts(zero):
 def test_select_one_workspace_across_both_paths():
     """One zero-filled workspace serves a run of selections ordered on one
     stream: the one-launch path (no prompt stage, at most 64 candidates,
-    whose last block clears the completion counter) and the three-launch
-    path (65 and 70 candidates) in turn, with and without a window, each
-    against the oracle; afterwards the counter is zero again."""
+    whose last block clears the completion counter), the two-level
+    one-launch path (65 to 256 candidates, which also clears one counter per
+    column group) and the three-launch path (300 candidates, ids repeated)
+    in turn, with and without a window, each against the oracle; afterwards
+    the counters are zero again."""
     wl = W.scaled(W.WORKLOADS["wan_kp4"], name="edge_ws", n_heads=2, frame_tokens=16,
                   page_frames=2, n_pages=70, chunk_frames=9, k_p=3)   # 32-token pages, 144 queries
     run = _pool_with_pages(wl, wl.n_pages)
@@ -395,11 +397,12 @@ def test_select_one_workspace_across_both_paths():
     host_means = run.oracle_means(range(wl.n_pages))
     rng = np.random.default_rng(5)
     cases = [(16, None), (64, None), (65, None), (5, [3, 7]), (70, [1]), (64, [0, 2, 4]),
-             (1, None), (64, None)]
+             (300, None), (1, None), (256, [5]), (64, None)]
     nbytes = max(wa.wa_select_workspace_bytes(run.L, q.shape[0], n) for n, _ in cases)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     for n_cand, recent in cases:
-        cand = rng.permutation(wl.n_pages)[:n_cand].astype(np.int32)
+        cand = (rng.permutation(wl.n_pages)[:n_cand] if n_cand <= wl.n_pages else
+                rng.integers(0, wl.n_pages, n_cand)).astype(np.int32)
         cd = torch.from_numpy(cand).cuda()
         k_p = min(wl.k_p, n_cand - (len(recent) if recent else 0))
         say("select one workspace", n_cand, recent)
@@ -413,7 +416,7 @@ def test_select_one_workspace_across_both_paths():
                                        cand=cand)["idx"]
         assert idx.cpu().numpy().tolist() == np.asarray(ref).tolist()
     torch.cuda.synchronize()
-    assert int(ws[:4].view(torch.int32).item()) == 0
+    assert not bool(ws[:256].any())
 
 
 @pytest.mark.parametrize("dtype,n_heads,head_dim,n_q,n_pages", [
@@ -421,11 +424,14 @@ def test_select_one_workspace_across_both_paths():
     (W.F32, 3, 128, 1500, 9),     # fp32: 96 vectors, two groups (64 + 32)
     (W.BF16, 3, 64, 1100, 12),    # bf16: 24 vectors, a group narrower than 64
     (W.BF16, 5, 128, 2000, 40),   # bf16: 80 vectors, two groups (64 + 16); 40 candidates
-], ids=["f32_h2_d64", "f32_h3_d128", "bf16_h3_d64", "bf16_h5_d128_40cand"])
+    (W.F32, 3, 128, 1500, 100),   # fp32, 100 candidates: the two-level path, 8-vector groups
+    (W.BF16, 3, 64, 1100, 90),    # bf16, 90 candidates: 24 vectors in 3 groups of 8
+], ids=["f32_h2_d64", "f32_h3_d128", "bf16_h3_d64", "bf16_h5_d128_40cand", "f32_h3_d128_100cand",
+        "bf16_h3_d64_90cand"])
 def test_select_layouts_and_shapes(dtype, n_heads, head_dim, n_q, n_pages):
-    """The one-launch selection over layouts whose column groups are narrower
-    than 64 vectors or ragged, with several row blocks, against the oracle
-    (ids, scores to 1e-12)."""
+    """The one-launch selection (and past 64 candidates the two-level one)
+    over layouts whose column groups are narrower than their width or ragged,
+    with several row blocks, against the oracle (ids, scores to 1e-12)."""
     base = W.WORKLOADS["tiny_f32"] if dtype == W.F32 else W.WORKLOADS["wan_kp4"]
     wl = W.scaled(base, name="sel_%s_%d_%d" % (dtype, n_heads, head_dim), dtype=dtype,
                   n_heads=n_heads, head_dim=head_dim, frame_tokens=16, page_frames=2,
