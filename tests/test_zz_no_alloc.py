@@ -1,8 +1,9 @@
 """wa_select_pages_noalloc -- the page selection with the library's fixed
 per-device workspace, for callers that cannot allocate -- against
-wa_select_pages with a caller-owned workspace, through the C ABI: two calls in
-a row, the second with a smaller input (fewer queries, an explicit list of
-fewer candidates with a repeated id), then the prompt stage.  The two entry
+wa_select_pages with a caller-owned workspace, through the C ABI: calls in a
+row, each with a smaller input than the one before (100 listed candidates,
+which take the two-level one-launch path; all 12 pages; fewer queries and 6
+listed candidates with a repeated id), then the prompt stage.  The two entry
 points run the same kernels in the same order, so ids and scores must be
 bit for bit equal.
 """
@@ -38,7 +39,10 @@ def test_noalloc_selection_equals_the_workspace_call():
     q, _, _ = W.chunk_qkv(wl, 0, 0)
     qd = to_device(q)
     small = torch.tensor([7, 2, 9, 2, 11, 0], dtype=torch.int32, device="cuda")
-    cases = [("all 12 pages, 1,200 queries", qd, None, wl.n_pages, 4),
+    many = torch.from_numpy(np.random.default_rng(3).integers(0, wl.n_pages, 100)
+                            .astype(np.int32)).cuda()
+    cases = [("100 listed candidates (ids repeated), 1,200 queries", qd, many, 100, 5),
+             ("all 12 pages, 1,200 queries", qd, None, wl.n_pages, 4),
              ("6 listed candidates, 300 queries", qd[:300].contiguous(), small, 6, 3)]
     for name, qq, cand, n_cand, k_p in cases:
         say("select noalloc:", name)
