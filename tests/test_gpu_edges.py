@@ -253,6 +253,33 @@ def test_select_exact_ties_between_pages():
     assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
 
 
+def test_select_at_the_limits():
+    """Selections at the library's limits, against the oracle: the widest row
+    (WA_MAX_ROW_ELEMS = 32 heads x 128) with 16 candidates (one launch, 32
+    column groups), 100 candidates (64 column groups of 8 vectors: more than
+    the two-level path's counters hold, so three launches) and 300 candidates
+    (three launches), and WA_MAX_CANDIDATES listed candidates (ids repeated)."""
+    wl = W.scaled(W.WORKLOADS["wan_kp4"], name="edge_wide_row", n_heads=32, frame_tokens=8,
+                  page_frames=2, n_pages=20, chunk_frames=30, k_p=5)   # 16-token pages, 240 queries
+    assert wl.n_heads * wl.head_dim == 4096
+    run = _pool_with_pages(wl, wl.n_pages)
+    q = W.chunk_qkv(wl, 0, 0)[0]
+    qd = to_device(q)
+    host_means = run.oracle_means(range(wl.n_pages))
+    rng = np.random.default_rng(11)
+    for n_cand in (16, 100, 300, 4096):
+        cand = (rng.permutation(wl.n_pages)[:n_cand] if n_cand <= wl.n_pages else
+                rng.integers(0, wl.n_pages, n_cand)).astype(np.int32)
+        say("select at the limits:", n_cand, "candidates, row of", wl.n_heads * wl.head_dim)
+        scores = torch.empty(n_cand, dtype=torch.float64, device="cuda")
+        idx = wa.wa_select_pages(run.L, qd, run.means, wl.k_p, cand=torch.from_numpy(cand).cuda(),
+                                 out_scores=scores)
+        ref = oracle.select_pages(q, host_means, wl.k_p, cand=cand)
+        assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
+        got = scores.cpu().numpy()
+        assert np.abs(got - ref["alpha"]).max() <= 1e-12 * max(1.0, np.abs(ref["alpha"]).max())
+
+
 @pytest.mark.parametrize("n_cand", [11, 1031])
 def test_select_fewer_valid_candidates_than_k_p(n_cand):
     wl = BF
