@@ -61,6 +61,25 @@ def test_attention_shapes(wl, n_q, n_ctx, n_own):
     assert np.abs(lse.cpu().double().numpy() - ref_lse).max() <= tol
 
 
+@pytest.mark.parametrize("n_q,n_ctx,n_own", [(300, 200, 70), (40, 3000, 40)],
+                         ids=["one_block_per_item", "split_launch"])
+def test_attention_widest_row(n_q, n_ctx, n_own):
+    """The widest row the library takes (WA_MAX_ROW_ELEMS = 32 heads x 128, an
+    8 KB token stride), bf16, against the oracle on both output dtypes and the
+    lse; the second shape has few items and many keys, so the launch splits."""
+    wl = W.scaled(BF, name="edge_wide_row_attn", n_heads=32)
+    assert wl.n_heads * wl.head_dim == 4096
+    q = rand_rows(wl, n_q, 21)
+    kc, vc = rand_rows(wl, n_ctx, 22), rand_rows(wl, n_ctx, 23)
+    ko, vo = rand_rows(wl, n_own, 24), rand_rows(wl, n_own, 25)
+    ref, ref_lse = oracle.attention(q, kc, vc, ko, vo, wl.softmax_scale)
+    for odt in (wa.WA_F32, wa.WA_BF16):
+        say("attention widest row", n_q, n_ctx, n_own, "out dtype", odt)
+        out, lse = attend(wl, q, kc, vc, ko, vo, odt=odt, lse=True)
+        assert np.abs(to_f64(out) - ref).max() <= 1e-2
+        assert np.abs(lse.cpu().double().numpy() - ref_lse).max() <= 1e-2
+
+
 @pytest.mark.parametrize("odt", [wa.WA_F32, wa.WA_BF16], ids=["f32_out", "bf16_out"])
 def test_attention_split_over_cus(odt):
     """Few (query block, head) items and many keys: the launch splits each
