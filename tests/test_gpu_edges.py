@@ -277,7 +277,8 @@ def test_select_at_the_limits():
     (WA_MAX_ROW_ELEMS = 32 heads x 128) with 16 candidates (one launch, 32
     column groups), 100 candidates (64 column groups of 8 vectors: more than
     the two-level path's counters hold, so three launches) and 300 candidates
-    (three launches), and WA_MAX_CANDIDATES listed candidates (ids repeated)."""
+    (three launches), and WA_MAX_CANDIDATES listed candidates (ids repeated);
+    then the gather of the last selection at that width, byte for byte."""
     wl = W.scaled(W.WORKLOADS["wan_kp4"], name="edge_wide_row", n_heads=32, frame_tokens=8,
                   page_frames=2, n_pages=20, chunk_frames=30, k_p=5)   # 16-token pages, 240 queries
     assert wl.n_heads * wl.head_dim == 4096
@@ -297,6 +298,12 @@ def test_select_at_the_limits():
         assert idx.cpu().numpy().tolist() == ref["idx"].tolist()
         got = scores.cpu().numpy()
         assert np.abs(got - ref["alpha"]).max() <= 1e-12 * max(1.0, np.abs(ref["alpha"]).max())
+    # the pages appended at this width gather byte for byte
+    k_ctx, v_ctx = wa.wa_gather(run.L, run.k_pool, run.v_pool, idx, wl.k_p)
+    torch.cuda.synchronize()
+    sel = idx.cpu().numpy()
+    assert to_bits(k_ctx).tobytes() == oracle.gather(np.stack([run.host_k[i] for i in range(wl.n_pages)]), sel).tobytes()
+    assert to_bits(v_ctx).tobytes() == oracle.gather(np.stack([run.host_v[i] for i in range(wl.n_pages)]), sel).tobytes()
 
 
 @pytest.mark.parametrize("n_cand", [11, 1031])
