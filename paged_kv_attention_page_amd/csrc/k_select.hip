@@ -50,8 +50,10 @@ namespace wa {
 
 // Workspace of wa_select_pages_noalloc: one fixed array per device, in the
 // library's device image, for callers that cannot allocate.  Every call on a
-// device shares it (calls that overlap on one device race); the selection
-// writes every entry it reads, so nothing needs clearing between calls.
+// device shares it (calls that overlap on one device race).  The selection
+// writes every entry it reads except the one-launch paths' completion
+// counters, which are zero when the image is loaded and which every call
+// leaves at zero, so nothing needs clearing between calls.
 static __device__ __align__(256) unsigned char scratch[WA_SELECT_NOALLOC_MAX_WORKSPACE];
 
 static constexpr int kMaxDevices = 64;
@@ -99,13 +101,15 @@ static constexpr int kWideRounds = 8;        // candidate rounds of partial dots
 // for the three launches; groups of 16 or 4 vectors measured slower, 2 or 4
 // rounds in flight no faster.)
 
-// One launch: at most kFusedMaxCand candidates, or with a prompt stage at
-// most kFusedMaxCand pages in all the past chunks (every chunk's pages are
-// scored, and the last block keeps those of the chunks the prompts select).
+// Two-level one launch: kFusedMaxCand + 1 ... kWideMaxCand candidates, no
+// prompt stage (and at most 63 column groups, checked with the plan).
 static bool select_wide(int32_t n_cand, int32_t n_chunks) {
     return n_chunks == 0 && n_cand > kFusedMaxCand && n_cand <= kWideMaxCand;
 }
 
+// One launch: at most kFusedMaxCand candidates, or with a prompt stage at
+// most kFusedMaxCand pages in all the past chunks (every chunk's pages are
+// scored, and the last block keeps those of the chunks the prompts select).
 static bool select_one_launch(int32_t n_cand, int32_t n_chunks, int32_t pages_per_chunk) {
     if (n_chunks == 0) return n_cand <= kFusedMaxCand;
     return (int64_t)n_chunks * pages_per_chunk <= kFusedMaxCand;
@@ -114,8 +118,9 @@ static bool select_one_launch(int32_t n_cand, int32_t n_chunks, int32_t pages_pe
 SelectWs select_workspace(int32_t dtype, int64_t hd, int32_t n_q, int32_t n_cand,
                           int32_t n_chunks, int32_t pages_per_chunk) {
     SelectWs w;
-    // [0, 256): the one-launch path's completion counter, zero between calls;
-    // the three-launch path leaves it alone
+    // [0, 256): the one-launch paths' completion counters (one; or, in two
+    // levels, the final one and one per column group), zero between calls;
+    // the three-launch path leaves them alone
     size_t off = 256;
     w.one_launch = select_one_launch(n_cand, n_chunks, pages_per_chunk);
     w.wide = false;
