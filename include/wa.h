@@ -204,7 +204,9 @@ wa_status wa_select_pages(const wa_layout *layout, const void *q, int32_t n_q,
  * (wa_select_workspace_bytes) exceeds WA_SELECT_NOALLOC_MAX_WORKSPACE ->
  * WA_ERR_UNSUPPORTED.  All calls on one GPU share the array, so calls that
  * overlap on one GPU (concurrent streams, threads) race; calls ordered on
- * one stream do not.
+ * one stream do not.  The call launches kernels only (no memset or copy), so
+ * it can be captured in a HIP graph; make one call on each device before
+ * capturing, so that the address look-up runs outside the capture.
  */
 #define WA_SELECT_NOALLOC_MAX_WORKSPACE (8u << 20)
 wa_status wa_select_pages_noalloc(const wa_layout *layout, const void *q, int32_t n_q,
