@@ -718,24 +718,49 @@ void k_attn_bf16(AttnArgs a) {
         const int geff = __builtin_amdgcn_readfirstlane(a.sp_plan[1]);
         const int total = __builtin_amdgcn_readfirstlane(a.sp_plan[2]);
         if (blk >= geff) return;
+        const int g0 = (int)((int64_t)blk * total / geff);
         const int g1 = (int)((int64_t)(blk + 1) * total / geff);
-        for (int g = (int)((int64_t)blk * total / geff); g < g1;) {
-            int lo = 0, hi = a.items;   // sp_prefix[lo] <= g < sp_prefix[hi]
+        auto item_of = [&](int g) -> int {   // sp_prefix[lo] <= g < sp_prefix[lo + 1]
+            int lo = 0, hi = a.items;
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
                 if (__builtin_amdgcn_readfirstlane(a.sp_prefix[mid]) <= g) lo = mid;
                 else hi = mid;
             }
+            return lo;
+        };
+        // Order of a run's pieces: a run that starts inside an item and
+        // reaches past its end begins at that item's end and takes its
+        // leading piece last (positions [start, g1), then [g0, start)).  The
+        // items of one head have lists of about the same length L, so every
+        // block of that head whose run holds an item boundary is then at list
+        // position (t mod L) or ((t - run) mod L) after t tiles, whatever the
+        // run's offset: the blocks of a head read the same tiles at about the
+        // same time and share one L2.  In position order each block sat at its
+        // own offset (3.5 GB fetched per Wan-shaped launch against 0.96 GB,
+        // 4 % slower).  The pieces and their slots are the same either way,
+        // so the results are too.
+        int start = g0;
+        if (g0 < g1) {
+            const int i0 = item_of(g0);
+            const int q0 = __builtin_amdgcn_readfirstlane(a.sp_prefix[i0]);
+            const int q1 = __builtin_amdgcn_readfirstlane(a.sp_prefix[i0 + 1]);
+            if (g0 > q0 && q1 < g1) start = q1;
+        }
+        for (int g = start, left = g1 - g0; left > 0;) {
+            const int end = g >= start ? g1 : start;
+            const int lo = item_of(g);
             const int p0 = __builtin_amdgcn_readfirstlane(a.sp_prefix[lo]);
             const int p1 = __builtin_amdgcn_readfirstlane(a.sp_prefix[lo + 1]);
-            const int e = p1 < g1 ? p1 : g1;
+            const int e = p1 < end ? p1 : end;
             __syncthreads();   // every wave is done with the previous piece's list
             load_list(lo, g - p0, e - p0);
             // (the arguments made uniform, as in the dense split: the compiler
             // then keeps them in scalar registers)
             segment(__builtin_amdgcn_readfirstlane(lo), 0, __builtin_amdgcn_readfirstlane(e - g),
                     __builtin_amdgcn_readfirstlane((g == p0 && e == p1) ? -1 : lo + blk));
-            g = e;
+            left -= e - g;
+            g = e == g1 ? g0 : e;
         }
         return;
     }
