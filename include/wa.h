@@ -21,6 +21,7 @@
  *                      share of a pooled attention map;
  *   wa_sparse_attention attention over those blocks only;
  *   wa_page_in/out     move a page between a pinned host tier and HBM;
+ *   wa_page_in_rows    page-in of a range of a page's token rows;
  *   wa_merge_attention combine attentions over two disjoint key sets.
  *
  * Sources (page title, section):
@@ -464,6 +465,22 @@ wa_status wa_page_in(const wa_layout *layout, const void *host_k, const void *ho
 wa_status wa_page_out(const wa_layout *layout, const void *k_pool, const void *v_pool,
                       int32_t slot, void *host_k, void *host_v, int32_t host_pages,
                       int32_t host_slot, void *stream);
+
+/*
+ * A page-in in parts (same tier passages as wa_page_in): token rows
+ * [row0, row0 + n_rows) of host page host_slot go to the same rows of pool
+ * slot `slot` (K, and V when given):
+ *   k_pool[slot][row0 + r] = host_k[host_slot][row0 + r],  0 <= r < n_rows.
+ * A page's rows are contiguous, so attention over the rows already copied
+ * (wa_block_attention on that row range of the slot, with wa_merge_attention
+ * combining the parts) can run while the rest of the page is copied; after
+ * the last part, the attention over the page is exact up to the merge's
+ * rounding.  Same arguments, conventions and errors as wa_page_in, plus:
+ * row0 < 0, n_rows < 1, row0 + n_rows > page_tokens -> WA_ERR_INVALID_ARG.
+ */
+wa_status wa_page_in_rows(const wa_layout *layout, const void *host_k, const void *host_v,
+                          int32_t host_pages, int32_t host_slot, void *k_pool, void *v_pool,
+                          int32_t slot, int32_t row0, int32_t n_rows, void *stream);
 
 /*
  * Merge of two attentions of the same queries over disjoint key sets A and B

@@ -11,7 +11,7 @@ stream.  The functions carry the C names:
 
 and the rest of ``wa.h`` under the same names: wa_select_window,
 wa_select_pages_noalloc, wa_paged_attention, wa_hsa_select,
-wa_sparse_attention, wa_page_in, wa_page_out, wa_merge_attention and the
+wa_sparse_attention, wa_page_in, wa_page_in_rows, wa_page_out, wa_merge_attention and the
 workspace-size queries.
 
 Host-side shape checks here only make sure every pointer handed to the
@@ -31,7 +31,7 @@ __all__ = ["WA_OK", "WA_ERR_INVALID_ARG", "WA_ERR_UNSUPPORTED", "WA_ERR_HIP", "W
            "wa_select_pages", "wa_select_window", "wa_gather", "wa_attention_workspace_bytes",
            "wa_block_attention", "wa_paged_attention", "hsa_shape", "wa_hsa_workspace_bytes",
            "wa_hsa_select", "wa_sparse_workspace_bytes", "wa_sparse_attention",
-           "wa_page_in", "wa_page_out", "wa_merge_attention", "wa_status_string",
+           "wa_page_in", "wa_page_in_rows", "wa_page_out", "wa_merge_attention", "wa_status_string",
            "use_library", "wa_select_pages_noalloc"]
 
 WA_OK, WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED, WA_ERR_HIP = 0, -1, -2, -3
@@ -134,6 +134,8 @@ def load_library():
                                         sz, p]
     lib.wa_page_in.argtypes = [L, p, p, i32, i32, p, p, i32, p]
     lib.wa_page_in.restype = i32
+    lib.wa_page_in_rows.argtypes = [L, p, p, i32, i32, p, p, i32, i32, i32, p]
+    lib.wa_page_in_rows.restype = i32
     lib.wa_page_out.argtypes = [L, p, p, i32, p, p, i32, i32, p]
     lib.wa_page_out.restype = i32
     lib.wa_merge_attention.argtypes = [L, i32, p, p, p, p, i32, p, p, p]
@@ -562,10 +564,19 @@ def _host_pool(t, name, L):
     return t.numel() // page
 
 
+def _dev_pool(k_pool, v_pool, L, slot):
+    """The HBM pools hold slot `slot` (the library checks slot < max_pages)."""
+    need = (int(slot) + 1) * L.page_tokens * L.row_elems if slot >= 0 else None
+    _need(k_pool, "k_pool", L.torch_dtype, need)
+    if v_pool is not None:
+        _need(v_pool, "v_pool", L.torch_dtype, need)
+
+
 def wa_page_in(L: Layout, host_k, host_v, host_slot: int, k_pool, v_pool, slot: int,
                stream=None):
     """k_pool[slot] = host_k[host_slot] (and V), queued on the copy engines."""
     lib = load_library()
+    _dev_pool(k_pool, v_pool, L, slot)
     n = _host_pool(host_k, "host_k", L)
     if host_v is not None and _host_pool(host_v, "host_v", L) != n:
         raise ValueError("host_k and host_v hold different page counts")
@@ -574,10 +585,26 @@ def wa_page_in(L: Layout, host_k, host_v, host_slot: int, k_pool, v_pool, slot: 
     _check(st, "wa_page_in")
 
 
+def wa_page_in_rows(L: Layout, host_k, host_v, host_slot: int, k_pool, v_pool, slot: int,
+                    row0: int, n_rows: int, stream=None):
+    """Token rows [row0, row0 + n_rows) of k_pool[slot] = the same rows of
+    host_k[host_slot] (and V), queued on the copy engines."""
+    lib = load_library()
+    _dev_pool(k_pool, v_pool, L, slot)
+    n = _host_pool(host_k, "host_k", L)
+    if host_v is not None and _host_pool(host_v, "host_v", L) != n:
+        raise ValueError("host_k and host_v hold different page counts")
+    st = lib.wa_page_in_rows(ctypes.byref(L), _ptr(host_k), _ptr(host_v), int(n), int(host_slot),
+                             _ptr(k_pool), _ptr(v_pool), int(slot), int(row0), int(n_rows),
+                             _stream(stream))
+    _check(st, "wa_page_in_rows")
+
+
 def wa_page_out(L: Layout, k_pool, v_pool, slot: int, host_k, host_v, host_slot: int,
                 stream=None):
     """host_k[host_slot] = k_pool[slot] (and V), queued on the copy engines."""
     lib = load_library()
+    _dev_pool(k_pool, v_pool, L, slot)
     n = _host_pool(host_k, "host_k", L)
     if host_v is not None and _host_pool(host_v, "host_v", L) != n:
         raise ValueError("host_k and host_v hold different page counts")

@@ -359,17 +359,19 @@ wa_status wa_merge_attention(const wa_layout *L, int32_t n_q, const float *out_a
 
 namespace {
 
-// One page of K (and V) between a pinned host pool and an HBM pool slot, on
-// the caller's stream (the copy engines move it; no kernel runs).
+// Token rows [row0, row0 + n_rows) of one page of K (and V) (the whole page:
+// 0, page_tokens) between a pinned host pool and an HBM pool slot, on the
+// caller's stream (the copy engines move it; no kernel runs).
 wa_status page_copy(const wa_layout *L, bool to_device, const void *host_k, const void *host_v,
                     int32_t host_pages, int32_t host_slot, const void *k_pool, const void *v_pool,
-                    int32_t slot, void *stream) {
+                    int32_t slot, int32_t row0, int32_t n_rows, void *stream) {
     const wa_status st = check_layout(L, true);
     if (st != WA_OK) return st;
     if (!host_k || !k_pool) return WA_ERR_INVALID_ARG;
     if ((host_v == nullptr) != (v_pool == nullptr)) return WA_ERR_INVALID_ARG;
     if (host_pages < 1 || host_slot < 0 || host_slot >= host_pages) return WA_ERR_INVALID_ARG;
     if (slot < 0 || slot >= L->max_pages) return WA_ERR_INVALID_ARG;
+    if (row0 < 0 || n_rows < 1 || (int64_t)row0 + n_rows > L->page_tokens) return WA_ERR_INVALID_ARG;
     if (!aligned16(host_k) || !aligned16(k_pool) || (host_v && !aligned16(host_v)) ||
         (v_pool && !aligned16(v_pool)))
         return WA_ERR_INVALID_ARG;
@@ -384,18 +386,19 @@ wa_status page_copy(const wa_layout *L, bool to_device, const void *host_k, cons
         }
         if (attr.type != hipMemoryTypeHost) return WA_ERR_INVALID_ARG;
     }
-    const size_t page_bytes =
-        (size_t)L->page_tokens * L->n_heads * L->head_dim * elem_bytes(L->dtype);
+    const size_t row_bytes = (size_t)L->n_heads * L->head_dim * elem_bytes(L->dtype);
+    const size_t page_bytes = (size_t)L->page_tokens * row_bytes;
+    const size_t first = (size_t)row0 * row_bytes, bytes = (size_t)n_rows * row_bytes;
     const hipMemcpyKind kind = to_device ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
-    const char *hk = (const char *)host_k + (size_t)host_slot * page_bytes;
-    const char *dk = (const char *)k_pool + (size_t)slot * page_bytes;
-    hipError_t e = to_device ? hipMemcpyAsync((void *)dk, hk, page_bytes, kind, (hipStream_t)stream)
-                             : hipMemcpyAsync((void *)hk, dk, page_bytes, kind, (hipStream_t)stream);
+    const char *hk = (const char *)host_k + (size_t)host_slot * page_bytes + first;
+    const char *dk = (const char *)k_pool + (size_t)slot * page_bytes + first;
+    hipError_t e = to_device ? hipMemcpyAsync((void *)dk, hk, bytes, kind, (hipStream_t)stream)
+                             : hipMemcpyAsync((void *)hk, dk, bytes, kind, (hipStream_t)stream);
     if (e != hipSuccess || !host_v) return from_hip(e);
-    const char *hv = (const char *)host_v + (size_t)host_slot * page_bytes;
-    const char *dv = (const char *)v_pool + (size_t)slot * page_bytes;
-    e = to_device ? hipMemcpyAsync((void *)dv, hv, page_bytes, kind, (hipStream_t)stream)
-                  : hipMemcpyAsync((void *)hv, dv, page_bytes, kind, (hipStream_t)stream);
+    const char *hv = (const char *)host_v + (size_t)host_slot * page_bytes + first;
+    const char *dv = (const char *)v_pool + (size_t)slot * page_bytes + first;
+    e = to_device ? hipMemcpyAsync((void *)dv, hv, bytes, kind, (hipStream_t)stream)
+                  : hipMemcpyAsync((void *)hv, dv, bytes, kind, (hipStream_t)stream);
     return from_hip(e);
 }
 
@@ -404,14 +407,22 @@ wa_status page_copy(const wa_layout *L, bool to_device, const void *host_k, cons
 wa_status wa_page_in(const wa_layout *L, const void *host_k, const void *host_v,
                      int32_t host_pages, int32_t host_slot, void *k_pool, void *v_pool,
                      int32_t slot, void *stream) {
-    return page_copy(L, true, host_k, host_v, host_pages, host_slot, k_pool, v_pool, slot, stream);
+    return page_copy(L, true, host_k, host_v, host_pages, host_slot, k_pool, v_pool, slot, 0,
+                     L ? L->page_tokens : 0, stream);
+}
+
+wa_status wa_page_in_rows(const wa_layout *L, const void *host_k, const void *host_v,
+                          int32_t host_pages, int32_t host_slot, void *k_pool, void *v_pool,
+                          int32_t slot, int32_t row0, int32_t n_rows, void *stream) {
+    return page_copy(L, true, host_k, host_v, host_pages, host_slot, k_pool, v_pool, slot, row0,
+                     n_rows, stream);
 }
 
 wa_status wa_page_out(const wa_layout *L, const void *k_pool, const void *v_pool, int32_t slot,
                       void *host_k, void *host_v, int32_t host_pages, int32_t host_slot,
                       void *stream) {
-    return page_copy(L, false, host_k, host_v, host_pages, host_slot, k_pool, v_pool, slot,
-                     stream);
+    return page_copy(L, false, host_k, host_v, host_pages, host_slot, k_pool, v_pool, slot, 0,
+                     L ? L->page_tokens : 0, stream);
 }
 
 const char *wa_status_string(wa_status s) {

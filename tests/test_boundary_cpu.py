@@ -450,19 +450,22 @@ def test_sparse_attention_rejects(lib):
 # host-memory page tier and the merge (rejected on the host: nothing runs)
 
 def _pin(lib, fn="wa_page_in", lay=None, hk=A, hv=B, host_pages=4, host_slot=1, kp=A, vp=B,
-         slot=2):
+         slot=2, row0=100, n_rows=3000):
     f = getattr(lib, fn)
     lay = None if lay == "null" else (lay if lay is not None else L())
     if fn == "wa_page_in":
         return f(lay, hk, hv, host_pages, host_slot, kp, vp, slot, None)
+    if fn == "wa_page_in_rows":
+        return f(lay, hk, hv, host_pages, host_slot, kp, vp, slot, row0, n_rows, None)
     return f(lay, kp, vp, slot, hk, hv, host_pages, host_slot, None)
 
 
-@pytest.mark.parametrize("fn", ["wa_page_in", "wa_page_out"])
+@pytest.mark.parametrize("fn", ["wa_page_in", "wa_page_out", "wa_page_in_rows"])
 def test_page_copy_rejects(lib, fn):
-    """Every argument rule of wa_page_in / wa_page_out, one bad argument per
-    call; the last case passes every other check with a host pointer that is
-    not pinned host memory (a stand-in address), so nothing is copied."""
+    """Every argument rule of wa_page_in / wa_page_out / wa_page_in_rows, one
+    bad argument per call; the last case passes every other check with a host
+    pointer that is not pinned host memory (a stand-in address), so nothing is
+    copied."""
     E = wa.WA_ERR_INVALID_ARG
     assert _pin(lib, fn, lay="null") == E
     assert _pin(lib, fn, hk=NULL) == E
@@ -477,6 +480,12 @@ def test_page_copy_rejects(lib, fn):
     assert _pin(lib, fn, lay=L(pt=0)) == E
     assert _pin(lib, fn, hk=MIS) == E
     assert _pin(lib, fn, vp=MIS) == E
+    if fn == "wa_page_in_rows":                             # the row range (page of 12,480)
+        assert _pin(lib, fn, row0=-1) == E
+        assert _pin(lib, fn, n_rows=0) == E
+        assert _pin(lib, fn, row0=12000, n_rows=481) == E
+        assert _pin(lib, fn, row0=0, n_rows=12481) == E
+        assert _pin(lib, fn, row0=12479, n_rows=1) == E     # in range: fails only on pinning
     assert _pin(lib, fn) == E                               # not pinned host memory
 
 

@@ -1,10 +1,11 @@
-"""Host-memory page tier: wa_page_out / wa_page_in between a pinned host pool
-and the HBM pool (bit-exact byte copies), wa_merge_attention against the
+"""Host-memory page tier: wa_page_out / wa_page_in / wa_page_in_rows between a
+pinned host pool and the HBM pool (bit-exact byte copies), wa_merge_attention against the
 oracle's merge and its attention over the union of the keys, and the tiered
 step: the selected pages that live in host memory are copied in on a second
 stream while the attention over the resident pages runs, then the attention
 over the copied pages and the merge -- held to the oracle's attention over
-all the selected pages.
+all the selected pages; also with the host page copied in row ranges, each
+attended as soon as it has landed.
 """
 import ctypes
 
@@ -71,6 +72,45 @@ def test_page_out_then_in_is_a_byte_copy():
     assert st == wa.WA_ERR_INVALID_ARG
 
 
+def test_page_in_rows_copies_those_rows_only():
+    """wa_page_in_rows in three uneven parts (and a K-only part): after each
+    part the copied rows are byte copies of the host page and the rest of
+    the slot is untouched."""
+    wl = SMALL                                     # 128-token pages
+    run = PoolRun(wl)
+    for j in range(wl.n_pages):
+        run.append(j)
+    hk, hv = _host_pool(wl, 2)
+    wa.wa_page_out(run.L, run.k_pool, run.v_pool, 5, hk, hv, 1)
+    torch.cuda.synchronize()
+    slot, P_t = 7, wl.page_tokens
+    run.k_pool[slot].fill_(-3.0)
+    run.v_pool[slot].fill_(-3.0)
+    before_k, before_v = _bits(run.k_pool[slot]).copy(), _bits(run.v_pool[slot]).copy()
+    done = 0
+    for r0, n in ((0, 37), (37, 63), (100, P_t - 100)):
+        say("page in rows", r0, "..", r0 + n, "of host page 1 -> slot", slot)
+        wa.wa_page_in_rows(run.L, hk, hv, 1, run.k_pool, run.v_pool, slot, r0, n)
+        torch.cuda.synchronize()
+        done = r0 + n
+        gk, gv = _bits(run.k_pool[slot]), _bits(run.v_pool[slot])
+        assert np.array_equal(gk[:done], run.host_k[5][:done].view(np.int16))
+        assert np.array_equal(gv[:done], run.host_v[5][:done].view(np.int16))
+        assert np.array_equal(gk[done:], before_k[done:])
+        assert np.array_equal(gv[done:], before_v[done:])
+    # K only, one row in the middle of slot 6
+    k6, v6 = _bits(run.k_pool[6]).copy(), _bits(run.v_pool[6]).copy()
+    say("page in row 64 of host page 1 (K only) -> slot 6")
+    wa.wa_page_in_rows(run.L, hk, None, 1, run.k_pool, None, 6, 64, 1)
+    torch.cuda.synchronize()
+    gk = _bits(run.k_pool[6])
+    assert np.array_equal(gk[64], run.host_k[5][64].view(np.int16))
+    assert np.array_equal(np.delete(gk, 64, axis=0), np.delete(k6, 64, axis=0))
+    assert np.array_equal(_bits(run.v_pool[6]), v6)
+    with pytest.raises(wa.WaError):
+        wa.wa_page_in_rows(run.L, hk, hv, 1, run.k_pool, run.v_pool, slot, 100, P_t - 99)
+
+
 def test_merge_matches_the_oracle():
     """Attention over the first 300 context keys and over the rest (with the
     own keys), merged, against the oracle's attention over all of them."""
@@ -134,6 +174,92 @@ def _tiered_step(run, q, ko, vo, idx, on_host, hk, hv, spare):
     out_b = wa.wa_paged_attention(L, qd, run.k_pool, run.v_pool, mis, len(slots), None, None,
                                   wl.softmax_scale, out_dtype=wa.WA_F32, lse=lse_b)
     return wa.wa_merge_attention(L, out_a, lse_a, out_b, lse_b, wa.WA_BF16)
+
+
+def _tiered_step_in_parts(run, q, ko, vo, idx, page, host_slot, hk, hv, spare, parts):
+    """Attention over pages idx, of which `page` lives in host memory: it is
+    copied into slot `spare` in `parts` row ranges on a second stream, each
+    followed by an event; the attention over the resident pages (with the own
+    keys) runs first, then the attention over each range as soon as it has
+    landed (wa_block_attention on those rows of the slot), each merged into
+    the running result."""
+    wl, L = run.wl, run.L
+    resident = [p for p in idx if p != page]
+    copy = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    copy.wait_stream(main)
+    bounds = [wl.page_tokens * i // parts for i in range(parts + 1)]
+    landed = []
+    with torch.cuda.stream(copy):
+        for r0, r1 in zip(bounds[:-1], bounds[1:]):
+            wa.wa_page_in_rows(L, hk, hv, host_slot, run.k_pool, run.v_pool, spare, r0, r1 - r0,
+                               stream=copy)
+            ev = torch.cuda.Event()
+            ev.record(copy)
+            landed.append(ev)
+    qd, kod, vod = to_device(q), to_device(ko), to_device(vo)
+    lse = torch.empty(wl.n_heads, q.shape[0], dtype=torch.float32, device="cuda")
+    res = torch.tensor(resident, dtype=torch.int32, device="cuda")
+    say("tiered step in", parts, "parts: resident", resident, "page", page, "into slot", spare)
+    out = wa.wa_paged_attention(L, qd, run.k_pool, run.v_pool, res, len(resident), kod, vod,
+                                wl.softmax_scale, out_dtype=wa.WA_F32, lse=lse)
+    for i, (r0, r1) in enumerate(zip(bounds[:-1], bounds[1:])):
+        main.wait_event(landed[i])
+        lse_b = torch.empty_like(lse)
+        out_b = wa.wa_block_attention(L, qd, run.k_pool[spare, r0:r1], run.v_pool[spare, r0:r1],
+                                      None, None, wl.softmax_scale, out_dtype=wa.WA_F32,
+                                      lse=lse_b)
+        if i == parts - 1:
+            return wa.wa_merge_attention(L, out, lse, out_b, lse_b, wa.WA_BF16)
+        lse_m = torch.empty_like(lse)
+        out = wa.wa_merge_attention(L, out, lse, out_b, lse_b, wa.WA_F32, lse=lse_m)
+        lse = lse_m
+
+
+@pytest.mark.parametrize("parts", [1, 3, 4])
+def test_tiered_step_in_parts_matches_the_oracle(parts):
+    wl = SMALL
+    run = PoolRun(wl)
+    for j in range(wl.n_pages):
+        run.append(j)
+    q, ko, vo = W.chunk_qkv(wl, 0, 0)
+    idx = wa.wa_select_pages(run.L, to_device(q), run.means, wl.k_p).cpu().numpy().tolist()
+    hk, hv = _host_pool(wl, 1)
+    wa.wa_page_out(run.L, run.k_pool, run.v_pool, idx[1], hk, hv, 0)
+    torch.cuda.synchronize()
+    run.k_pool[idx[1]].zero_()
+    run.v_pool[idx[1]].zero_()
+    spare = [p for p in range(wl.max_pages) if p not in idx][0]
+    out = _tiered_step_in_parts(run, q, ko, vo, idx, idx[1], 0, hk, hv, spare, parts)
+    torch.cuda.synchronize()
+    k_ctx = np.concatenate([run.host_k[p] for p in idx])
+    v_ctx = np.concatenate([run.host_v[p] for p in idx])
+    ref, _ = oracle.attention(q, k_ctx, v_ctx, ko, vo, wl.softmax_scale)
+    assert np.abs(to_f64(out) - ref).max() <= attention_tolerance(wl)
+
+
+def test_tiered_step_in_parts_full_size():
+    """wan_kp4 at full size, the first selected page copied in 4 parts during
+    the attention; sampled rows against the oracle."""
+    wl = W.WORKLOADS["wan_kp4"]
+    run = PoolRun(wl)
+    for j in range(wl.n_pages):
+        run.append(j)
+    q, ko, vo = W.chunk_qkv(wl, 0, 0)
+    idx = wa.wa_select_pages(run.L, to_device(q), run.means, wl.k_p).cpu().numpy().tolist()
+    hk, hv = _host_pool(wl, 1)
+    wa.wa_page_out(run.L, run.k_pool, run.v_pool, idx[0], hk, hv, 0)
+    torch.cuda.synchronize()
+    run.k_pool[idx[0]].zero_()
+    run.v_pool[idx[0]].zero_()
+    spare = [p for p in range(wl.max_pages) if p not in idx][0]
+    out = _tiered_step_in_parts(run, q, ko, vo, idx, idx[0], 0, hk, hv, spare, 4)
+    torch.cuda.synchronize()
+    rows = rows_sample(wl.n_q, 10)
+    k_ctx = np.concatenate([run.host_k[p] for p in idx])
+    v_ctx = np.concatenate([run.host_v[p] for p in idx])
+    ref, _ = oracle.attention(q, k_ctx, v_ctx, ko, vo, wl.softmax_scale, rows=rows)
+    assert np.abs(to_f64(out)[rows] - ref).max() <= attention_tolerance(wl)
 
 
 def test_tiered_step_matches_the_oracle():
