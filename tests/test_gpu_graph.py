@@ -128,3 +128,81 @@ def test_graph_replays_of_a_step_equal_the_eager_step():
             first_out = got[4]
         else:   # the replay read this step's inputs, not the captured ones
             assert not np.array_equal(first_out, got[4])
+
+
+def test_graph_replays_of_the_sparse_branch_equal_the_eager_calls():
+    """wa_hsa_select then wa_sparse_attention (plan, tile-list attention,
+    merge) captured in one HIP graph, replayed with new queries, against the
+    eager calls: tile lists, counts, output and lse bit for bit.  The shape
+    (12 items of up to 1,005 tiles on all CUs) takes the split launch."""
+    H, d, n_q, n_ctx, n_own = 4, 128, 700, 64 * 1000, 300
+    L = wa.layout(wa.WA_BF16, H, d)
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(11)
+    q = torch.empty((n_q, H, d), dtype=torch.bfloat16, device=dev)
+    k_ctx = torch.randn((n_ctx, H, d), device=dev, generator=g).to(torch.bfloat16)
+    v_ctx = torch.randn((n_ctx, H, d), device=dev, generator=g).to(torch.bfloat16)
+    k_own = torch.randn((n_own, H, d), device=dev, generator=g).to(torch.bfloat16)
+    v_own = torch.randn((n_own, H, d), device=dev, generator=g).to(torch.bfloat16)
+    tau = torch.tensor([0.5, 0.7, 0.9, 0.95], dtype=torch.float64, device=dev)
+    _, items, n_tiles = wa.hsa_shape(L, n_q, n_ctx, n_own)
+    tiles = torch.empty((items, n_tiles), dtype=torch.int32, device=dev)
+    count = torch.empty(items, dtype=torch.int32, device=dev)
+    ws_sel = torch.empty(max(16, wa.wa_hsa_workspace_bytes(L, n_q, n_ctx, n_own)),
+                         dtype=torch.uint8, device=dev)
+    ws_att = torch.empty(max(16, wa.wa_sparse_workspace_bytes(L, n_q, n_ctx, n_own)),
+                         dtype=torch.uint8, device=dev)
+    out = torch.empty((n_q, H, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((H, n_q), dtype=torch.float32, device=dev)
+    outputs = (tiles, count, out, lse)
+
+    def branch():
+        wa.wa_hsa_select(L, q, k_ctx, k_own, tau, sel_tiles=tiles, sel_count=count,
+                         want_gini=False, workspace=ws_sel)
+        wa.wa_sparse_attention(L, q, k_ctx, v_ctx, k_own, v_own, tiles, count,
+                               out_dtype=wa.WA_BF16, out=out, lse=lse, workspace=ws_att)
+
+    def load(r):
+        # queries with a shared direction, so the pooled map is concentrated
+        # and the heads keep different numbers of blocks
+        gr = torch.Generator(device=dev).manual_seed(100 + r)
+        x = torch.randn((n_q, H, d), device=dev, generator=gr)
+        q.copy_((x + 2.0 * k_ctx[:1].float()).to(torch.bfloat16))
+
+    def junk():
+        tiles.fill_(-9)
+        count.fill_(-9)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+
+    load(0)
+    say("graph: eager sparse branch")
+    branch()
+    torch.cuda.synchronize()
+    assert int(ws_att[:4].view(torch.int32)[0]) == 1, "the shape should take the split launch"
+    say("graph: capture of the sparse branch")
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        branch()
+    torch.cuda.synchronize()
+    first = None
+    for r in range(3):
+        load(r)
+        junk()
+        say("graph: sparse replay", r)
+        gr.replay()
+        torch.cuda.synchronize()
+        got = [_bits(t) for t in outputs]
+        junk()
+        say("graph: eager sparse branch", r)
+        branch()
+        torch.cuda.synchronize()
+        ref = [_bits(t) for t in outputs]
+        for name, a, b in zip(("tiles", "count", "out", "lse"), got, ref):
+            assert np.array_equal(a, b), "replay %d: %s differs from the eager calls" % (r, name)
+        assert np.all(got[1] >= 1) and np.all(got[1] <= n_tiles)
+        assert not torch.isnan(out).any().item()
+        if first is None:
+            first = got[2]
+        else:
+            assert not np.array_equal(first, got[2])
